@@ -1,0 +1,158 @@
+/*
+ * jetfire.h -- C ABI of the MI355X (gfx950) per-block INT8 data-flow library
+ * (libjetfire.so).
+ *
+ * Method: "Jetfire: Efficient and Accurate Transformer Pretraining with INT8
+ * Data Flow and Per-Block Quantization" (scime.ai summary of arXiv
+ * 2403.12422).  Its one-line summary and "Approach" section describe the
+ * data flow implemented here: every linear and non-linear operator reads and
+ * writes INT8 tensors that carry one scale factor per 32x32 block, the
+ * quantization is done on-chip by the producing kernel, and the weight
+ * gradient is an INT8 GEMM with per-block scales as well.  Its "Problem"
+ * section names the non-linear operators as memory-bound.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Matrices are row-major.  A "leading dimension" (ld*) is the distance,
+ *    in elements, between the starts of consecutive stored rows.
+ *  - Every row and column count is a multiple of 32.  Block (bi, bj) covers
+ *    rows 32bi..32bi+31 and columns 32bj..32bj+31 of the stored matrix.
+ *  - A scale grid of a stored R x C matrix is binary32 [R/32][C/32],
+ *    row-major and contiguous (its leading dimension is C/32).
+ *  - Per-block rule (the readings of the pages used throughout):
+ *        s = fl(max|x| / 127)               one IEEE binary32 division
+ *        q = clamp(rne(fl(x / s)), -127, 127)
+ *    and a block whose s is zero (all zeros, or max|x|/127 underflows) has
+ *    q = 0 everywhere.  Dequantized value: fl(s * q).
+ *  - Pointers are DEVICE pointers (hipMalloc'd or any device-accessible
+ *    allocation), except that nothing is dereferenced before validation.
+ *    The caller owns every buffer; the library never allocates, frees,
+ *    copies to the host or synchronizes.  Work is enqueued on `stream`
+ *    (0 = the null stream) and is asynchronous; outputs are fully written.
+ *  - Validation runs on the host before any HIP call and reports the first
+ *    failing condition:
+ *        JF_ERR_NULL   a required pointer is NULL (the pointers of an empty
+ *                      matrix may be NULL)
+ *        JF_ERR_SHAPE  a size is negative or not a multiple of 32
+ *        JF_ERR_LD     a leading dimension is below the row length, or its
+ *                      row pitch is not a multiple of 16 bytes
+ *        JF_ERR_ALIGN  a matrix base is not 16-byte aligned, or a scale grid
+ *                      base is not 4-byte aligned
+ *        JF_ERR_DTYPE  an unknown element type / output kind
+ *        JF_ERR_ARG    a transpose flag other than 0 or 1
+ *        JF_ERR_ALIAS  an output overlaps an input or another output
+ *        JF_ERR_HIP    the kernel launch failed (hipGetLastError)
+ *    A size of zero is valid: nothing is launched for an empty output, and a
+ *    GEMM with K = 0 writes zeros (binary32) or zero codes and scales.
+ *  - Inputs must be finite; NaN or Inf inputs give unspecified outputs.
+ *  - Entry points keep no state and are safe to call from several threads.
+ */
+#ifndef JETFIRE_H
+#define JETFIRE_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define JF_ABI_VERSION 1
+
+#ifndef JF_API
+#define JF_API __attribute__((visibility("default")))
+#endif
+
+typedef enum jf_status {
+    JF_OK = 0,
+    JF_ERR_NULL = 1,
+    JF_ERR_SHAPE = 2,
+    JF_ERR_LD = 3,
+    JF_ERR_ALIGN = 4,
+    JF_ERR_DTYPE = 5,
+    JF_ERR_ARG = 6,
+    JF_ERR_ALIAS = 7,
+    JF_ERR_HIP = 8
+} jf_status;
+
+/* Element type of a high-precision input. */
+typedef enum jf_dtype { JF_F32 = 0, JF_BF16 = 1 } jf_dtype;
+
+/* Output kind of the GEMM. */
+typedef enum jf_out { JF_OUT_I8 = 0, JF_OUT_F32 = 1 } jf_out;
+
+/*
+ * jf_quantize_block -- per-block INT8 quantization of a high-precision matrix.
+ * Pages: one-line summary and "Approach" (INT8 tensors with one scale per
+ * 32x32 block, quantization on-chip).
+ *
+ *   xt    JF_F32 (binary32) or JF_BF16 (bfloat16; each value is widened
+ *         exactly to binary32 first)
+ *   x     rows x cols input, leading dimension ldx (elements of xt)
+ *   q     rows x cols int8 codes, leading dimension ldq
+ *   s     (rows/32) x (cols/32) binary32 scales, contiguous
+ * Codes and scales are bit-exact with the per-block rule above.
+ */
+JF_API jf_status jf_quantize_block(jf_dtype xt, const void *x, int64_t ldx, int64_t rows, int64_t cols,
+                            int8_t *q, int64_t ldq, float *s, hipStream_t stream);
+
+/*
+ * jf_gemm_i8_blockscaled -- C[M x N] = op(A)[M x K] . op(B)[K x N] on INT8
+ * codes with per-block scales.  Pages: "Approach" (linear operators in the
+ * INT8 data flow; the weight gradient is also INT8 with per-block scales).
+ *
+ *   transA  0: A stored M x K (lda >= K);  1: A stored K x M (lda >= M)
+ *   transB  0: B stored K x N (ldb >= N);  1: B stored N x K (ldb >= K)
+ *   sA, sB  scale grids of A and B in their STORED orientation
+ *           (e.g. transA = 1: sA is [K/32][M/32])
+ *   out     JF_OUT_F32: C is binary32, ldc >= N, sC ignored (may be NULL)
+ *           JF_OUT_I8:  C is int8 codes, ldc >= N, sC is [M/32][N/32]
+ * Numerics.  For each output block (I, J) and each 32-deep k-block kappa in
+ * ascending order: P = exact int32 sum of 32 code products; sigma =
+ * fl(sA[I,kappa] * sB[kappa,J]); acc = fma(sigma, (float)P, acc) in binary32,
+ * starting from +0.  JF_OUT_F32 stores acc; JF_OUT_I8 requantizes each
+ * 32x32 output block with the per-block rule before it leaves the chip.
+ * For a linear layer with W stored K x N (in x out features):
+ *   forward Y = X W (0,0);  dgrad dX = dY W^T (0,1);  wgrad dW = X^T dY (1,0).
+ */
+JF_API jf_status jf_gemm_i8_blockscaled(int transA, int transB, int64_t M, int64_t N, int64_t K,
+                                 const int8_t *A, int64_t lda, const float *sA,
+                                 const int8_t *B, int64_t ldb, const float *sB,
+                                 jf_out out, void *C, int64_t ldc, float *sC,
+                                 hipStream_t stream);
+
+/*
+ * jf_requant_block -- per-block requantization of a binary32 matrix: the
+ * stand-alone form of the GEMM's requantizing epilogue (pages: "Approach",
+ * quantization applied on-chip by the producer).  Same rule, same layout as
+ * jf_quantize_block with xt = JF_F32.
+ */
+JF_API jf_status jf_requant_block(const float *x, int64_t ldx, int64_t rows, int64_t cols,
+                           int8_t *q, int64_t ldq, float *s, hipStream_t stream);
+
+/*
+ * jf_gelu_i8 -- INT8-in / INT8-out GELU.  Pages: "Problem" (non-linear
+ * operators are memory-bound) and "Approach" (they too read and write INT8
+ * with per-block scales).
+ *
+ *   q, s    rows x cols input codes (ldq) and their scale grid
+ *   qo, so  rows x cols output codes (ldqo) and their scale grid
+ * Per block: x = fl(s*q); g = x * Phi(x) with Phi the standard normal CDF
+ * (erf form of GELU), computed in binary32; then the per-block rule on g.
+ * Matches a binary64 evaluation of g to within 1 code on a few elements in
+ * 10^4 and scales to within a few ulp.  In-place operation is rejected.
+ */
+JF_API jf_status jf_gelu_i8(const int8_t *q, int64_t ldq, const float *s, int64_t rows, int64_t cols,
+                     int8_t *qo, int64_t ldqo, float *so, hipStream_t stream);
+
+/* Human-readable name of a status code (static storage). */
+JF_API const char *jf_status_str(jf_status status);
+
+/* JF_ABI_VERSION of the built library. */
+JF_API int jf_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* JETFIRE_H */

@@ -9,10 +9,9 @@ from __future__ import annotations
 
 import importlib
 
-__all__ = ["jetfire", "inputs", "quantize_block", "requant_block", "gemm_i8_blockscaled",
-           "gelu_i8", "dequantize"]
+__all__ = ["jetfire", "inputs", "quantize_block", "requant_block", "gemm_i8_blockscaled", "gelu_i8"]
 
-_BINDING_NAMES = {"quantize_block", "requant_block", "gemm_i8_blockscaled", "gelu_i8", "dequantize"}
+_BINDING_NAMES = {"quantize_block", "requant_block", "gemm_i8_blockscaled", "gelu_i8"}
 
 
 def __getattr__(name):

@@ -1,0 +1,134 @@
+// abi.hip -- the C ABI of libjetfire (declared in include/jetfire.h).
+//
+// Every entry point validates its arguments on the host, in the order the
+// header lists the status codes, before any HIP call, then enqueues its
+// kernels on the caller's stream.  Nothing here allocates or synchronizes.
+#include "../../include/jetfire.h"
+#include "jf_launch.h"
+
+#include <stdint.h>
+
+namespace {
+
+constexpr int64_t kB = 32;
+
+struct Range {
+    uintptr_t lo, hi;  // [lo, hi)
+};
+
+// Bytes spanned by a rows x cols matrix of elt-byte elements with leading
+// dimension ld (empty for an empty matrix).
+Range span(const void *p, int64_t rows, int64_t cols, int64_t ld, int64_t elt) {
+    if (rows <= 0 || cols <= 0) return {0, 0};
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return {lo, lo + (uintptr_t)(((rows - 1) * ld + cols) * elt)};
+}
+
+bool overlap(Range a, Range b) { return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi; }
+
+bool shape_ok(int64_t v) { return v >= 0 && v % kB == 0 && v <= (int64_t(1) << 30); }
+
+// ld must cover the row and give a 16-byte row pitch.
+bool ld_ok(int64_t ld, int64_t row_len, int64_t elt) {
+    return ld >= row_len && ld <= (int64_t(1) << 36) && (ld * elt) % 16 == 0;
+}
+
+bool aligned(const void *p, uintptr_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }  // NULL is aligned
+
+jf_status hip_status(hipError_t e) { return e == hipSuccess ? JF_OK : JF_ERR_HIP; }
+
+// A pointer is required unless its matrix is empty (torch hands out NULL for
+// empty tensors).  Negative sizes count as non-empty here and are rejected
+// by the shape check that follows.
+bool missing(const void *p, int64_t rows, int64_t cols) { return !p && !(rows == 0 || cols == 0); }
+
+}  // namespace
+
+extern "C" {
+
+int jf_abi_version(void) { return JF_ABI_VERSION; }
+
+const char *jf_status_str(jf_status st) {
+    switch (st) {
+        case JF_OK: return "ok";
+        case JF_ERR_NULL: return "null pointer";
+        case JF_ERR_SHAPE: return "size negative or not a multiple of 32";
+        case JF_ERR_LD: return "leading dimension below row length or row pitch not a multiple of 16 bytes";
+        case JF_ERR_ALIGN: return "pointer misaligned (matrices 16 bytes, scales 4 bytes)";
+        case JF_ERR_DTYPE: return "unknown element type or output kind";
+        case JF_ERR_ARG: return "transpose flag not 0 or 1";
+        case JF_ERR_ALIAS: return "an output overlaps an input or another output";
+        case JF_ERR_HIP: return "HIP kernel launch failed";
+    }
+    return "unknown status";
+}
+
+jf_status jf_quantize_block(jf_dtype xt, const void *x, int64_t ldx, int64_t rows, int64_t cols, int8_t *q,
+                            int64_t ldq, float *s, hipStream_t stream) {
+    if (missing(x, rows, cols) || missing(q, rows, cols) || missing(s, rows, cols)) return JF_ERR_NULL;
+    if (!shape_ok(rows) || !shape_ok(cols)) return JF_ERR_SHAPE;
+    if (xt != JF_F32 && xt != JF_BF16) return JF_ERR_DTYPE;
+    const int64_t elt = xt == JF_F32 ? 4 : 2;
+    if (!ld_ok(ldx, cols, elt) || !ld_ok(ldq, cols, 1)) return JF_ERR_LD;
+    if (!aligned(x, 16) || !aligned(q, 16) || !aligned(s, 4)) return JF_ERR_ALIGN;
+    const Range rx = span(x, rows, cols, ldx, elt), rq = span(q, rows, cols, ldq, 1);
+    const Range rs = span(s, rows / kB, cols / kB, cols / kB, 4);
+    if (overlap(rx, rq) || overlap(rx, rs) || overlap(rq, rs)) return JF_ERR_ALIAS;
+    if (rows == 0 || cols == 0) return JF_OK;
+    if (xt == JF_F32)
+        return hip_status(jf::launch_quantize_f32(static_cast<const float *>(x), ldx, rows, cols, q, ldq, s, stream));
+    return hip_status(jf::launch_quantize_bf16(static_cast<const uint16_t *>(x), ldx, rows, cols, q, ldq, s, stream));
+}
+
+jf_status jf_requant_block(const float *x, int64_t ldx, int64_t rows, int64_t cols, int8_t *q, int64_t ldq,
+                           float *s, hipStream_t stream) {
+    return jf_quantize_block(JF_F32, x, ldx, rows, cols, q, ldq, s, stream);
+}
+
+jf_status jf_gemm_i8_blockscaled(int transA, int transB, int64_t M, int64_t N, int64_t K, const int8_t *A,
+                                 int64_t lda, const float *sA, const int8_t *B, int64_t ldb, const float *sB,
+                                 jf_out out, void *C, int64_t ldc, float *sC, hipStream_t stream) {
+    if (missing(A, M, K) || missing(sA, M, K) || missing(B, K, N) || missing(sB, K, N) || missing(C, M, N))
+        return JF_ERR_NULL;
+    if (out == JF_OUT_I8 && missing(sC, M, N)) return JF_ERR_NULL;
+    if (!shape_ok(M) || !shape_ok(N) || !shape_ok(K)) return JF_ERR_SHAPE;
+    if (out != JF_OUT_I8 && out != JF_OUT_F32) return JF_ERR_DTYPE;
+    if ((transA != 0 && transA != 1) || (transB != 0 && transB != 1)) return JF_ERR_ARG;
+    // stored shapes
+    const int64_t a_rows = transA ? K : M, a_cols = transA ? M : K;
+    const int64_t b_rows = transB ? N : K, b_cols = transB ? K : N;
+    const int64_t c_elt = out == JF_OUT_F32 ? 4 : 1;
+    if (!ld_ok(lda, a_cols, 1) || !ld_ok(ldb, b_cols, 1) || !ld_ok(ldc, N, c_elt)) return JF_ERR_LD;
+    if (!aligned(A, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(sA, 4) || !aligned(sB, 4) ||
+        (out == JF_OUT_I8 && !aligned(sC, 4)))
+        return JF_ERR_ALIGN;
+    const Range ra = span(A, a_rows, a_cols, lda, 1), rb = span(B, b_rows, b_cols, ldb, 1);
+    const Range rsa = span(sA, a_rows / kB, a_cols / kB, a_cols / kB, 4);
+    const Range rsb = span(sB, b_rows / kB, b_cols / kB, b_cols / kB, 4);
+    const Range rc = span(C, M, N, ldc, c_elt);
+    const Range rsc = out == JF_OUT_I8 ? span(sC, M / kB, N / kB, N / kB, 4) : Range{0, 0};
+    for (Range in : {ra, rb, rsa, rsb})
+        if (overlap(rc, in) || overlap(rsc, in)) return JF_ERR_ALIAS;
+    if (overlap(rc, rsc)) return JF_ERR_ALIAS;
+    if (M == 0 || N == 0) return JF_OK;
+    return hip_status(jf::launch_gemm(transA, transB, M, N, K, A, lda, sA, B, ldb, sB, out == JF_OUT_I8, C, ldc,
+                                      sC, stream));
+}
+
+jf_status jf_gelu_i8(const int8_t *q, int64_t ldq, const float *s, int64_t rows, int64_t cols, int8_t *qo,
+                     int64_t ldqo, float *so, hipStream_t stream) {
+    if (missing(q, rows, cols) || missing(s, rows, cols) || missing(qo, rows, cols) || missing(so, rows, cols))
+        return JF_ERR_NULL;
+    if (!shape_ok(rows) || !shape_ok(cols)) return JF_ERR_SHAPE;
+    if (!ld_ok(ldq, cols, 1) || !ld_ok(ldqo, cols, 1)) return JF_ERR_LD;
+    if (!aligned(q, 16) || !aligned(qo, 16) || !aligned(s, 4) || !aligned(so, 4)) return JF_ERR_ALIGN;
+    const Range rq = span(q, rows, cols, ldq, 1), rqo = span(qo, rows, cols, ldqo, 1);
+    const Range rs = span(s, rows / kB, cols / kB, cols / kB, 4), rso = span(so, rows / kB, cols / kB, cols / kB, 4);
+    for (Range in : {rq, rs})
+        if (overlap(rqo, in) || overlap(rso, in)) return JF_ERR_ALIAS;
+    if (overlap(rqo, rso)) return JF_ERR_ALIAS;
+    if (rows == 0 || cols == 0) return JF_OK;
+    return hip_status(jf::launch_gelu(q, ldq, s, rows, cols, qo, ldqo, so, stream));
+}
+
+}  // extern "C"

@@ -53,6 +53,18 @@ def activation(workload_id: int, index: int, rows: int, cols: int,
     return x
 
 
+def codes(workload_id: int, tag: int, index: int, rows: int, cols: int) -> np.ndarray:
+    """Uniform int8 codes in [-127, 127] (random operands for GEMM tests)."""
+    return rng(workload_id, tag, index).integers(-127, 128, size=(rows, cols)).astype(np.int8)
+
+
+def scales(workload_id: int, tag: int, index: int, rows: int, cols: int) -> np.ndarray:
+    """Positive float32 values spread over three decades (random scale grids)."""
+    g = rng(workload_id, tag, index)
+    mant = g.random((rows, cols)) * 1.5 + 0.5
+    return (mant * 10.0 ** g.integers(-4, -1, size=(rows, cols))).astype(np.float32)
+
+
 def n_outliers(fraction: float, cols: int) -> int:
     return int(round(fraction * cols))
 

@@ -1,0 +1,106 @@
+"""C ABI host logic, without a GPU.
+
+The library must load, export every symbol include/jetfire.h declares, and
+reject bad arguments with the documented status codes BEFORE any HIP call
+(the header promises validation first), so every case here returns without
+touching a device.  Pointers below are fake addresses; none is dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from int8_block_quantized_amd import jetfire as jf
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "jetfire.h")
+
+P = ctypes.c_void_p
+BASE = 0x7f0000000000          # fake, 256-byte aligned addresses
+A_, B_, SA, SB, C_, SC = (P(BASE + i * 0x10000000) for i in range(6))
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return re.findall(r"JF_API\s+[\w\s\*]+?\b(jf_\w+)\s*\(", text)
+
+
+def test_exports_every_declared_symbol():
+    names = declared_symbols()
+    assert set(names) == set(jf.EXPORTS)
+    for n in names:
+        assert hasattr(jf.lib, n), n
+
+
+def test_version_and_status_strings():
+    assert jf.abi_version() == 1
+    for st in range(0, 9):
+        assert jf.status_str(st) and jf.status_str(st) != "unknown status"
+    assert jf.status_str(99) == "unknown status"
+
+
+def gemm(ta=0, tb=0, M=64, N=64, K=64, A=A_, lda=None, sA=SA, B=B_, ldb=None, sB=SB, out=jf.JF_OUT_I8,
+         C=C_, ldc=None, sC=SC):
+    lda = lda if lda is not None else (M if ta else K)
+    ldb = ldb if ldb is not None else (K if tb else N)
+    ldc = ldc if ldc is not None else N
+    return jf.lib.jf_gemm_i8_blockscaled(ta, tb, M, N, K, A, lda, sA, B, ldb, sB, out, C, ldc, sC, None)
+
+
+def test_gemm_validation_codes():
+    assert gemm(A=None) == jf.JF_ERR_NULL
+    assert gemm(sB=None) == jf.JF_ERR_NULL
+    assert gemm(sC=None) == jf.JF_ERR_NULL                      # required for INT8 output
+    assert gemm(M=0, A=None, C=None, sC=None) == jf.JF_OK        # empty output: nothing to do
+    assert gemm(M=48) == jf.JF_ERR_SHAPE
+    assert gemm(K=-32) == jf.JF_ERR_SHAPE
+    assert gemm(out=7) == jf.JF_ERR_DTYPE
+    assert gemm(ta=2) == jf.JF_ERR_ARG
+    assert gemm(tb=-1) == jf.JF_ERR_ARG
+    assert gemm(lda=32) == jf.JF_ERR_LD                          # below the row length
+    assert gemm(ldb=72) == jf.JF_ERR_LD                          # pitch not 16-byte multiple
+    assert gemm(out=jf.JF_OUT_F32, ldc=66, sC=None) == jf.JF_ERR_LD   # 264-byte pitch
+    assert gemm(A=P(BASE + 8)) == jf.JF_ERR_ALIGN
+    assert gemm(sA=P(BASE + 0x10000002)) == jf.JF_ERR_ALIGN
+    # output codes overlapping the A operand
+    assert gemm(C=P(BASE + 0x100)) == jf.JF_ERR_ALIAS
+    # output scales overlapping the output codes
+    assert gemm(sC=P(BASE + 4 * 0x10000000 + 64)) == jf.JF_ERR_ALIAS
+
+
+def test_quantize_validation_codes():
+    q = jf.lib.jf_quantize_block
+    x, qq, s = P(BASE), P(BASE + 0x10000000), P(BASE + 0x20000000)
+    assert q(jf.JF_F32, None, 64, 64, 64, qq, 64, s, None) == jf.JF_ERR_NULL
+    assert q(jf.JF_F32, x, 64, 64, 40, qq, 64, s, None) == jf.JF_ERR_SHAPE
+    assert q(3, x, 64, 64, 64, qq, 64, s, None) == jf.JF_ERR_DTYPE
+    assert q(jf.JF_F32, x, 32, 64, 64, qq, 64, s, None) == jf.JF_ERR_LD
+    assert q(jf.JF_BF16, x, 68, 64, 64, qq, 64, s, None) == jf.JF_ERR_LD    # 136 B pitch
+    assert q(jf.JF_F32, x, 64, 64, 64, qq, 72, s, None) == jf.JF_ERR_LD     # 72 B pitch
+    assert q(jf.JF_F32, P(BASE + 4), 64, 64, 64, qq, 64, s, None) == jf.JF_ERR_ALIGN
+    assert q(jf.JF_F32, x, 64, 64, 64, qq, 64, P(BASE + 0x20000002), None) == jf.JF_ERR_ALIGN
+    assert q(jf.JF_F32, x, 64, 64, 64, P(BASE + 1024), 64, s, None) == jf.JF_ERR_ALIAS
+    # empty input: valid, nothing launched, NULL allowed
+    assert q(jf.JF_F32, x, 64, 0, 64, qq, 64, s, None) == jf.JF_OK
+    assert q(jf.JF_F32, None, 64, 0, 64, None, 64, None, None) == jf.JF_OK
+    r = jf.lib.jf_requant_block
+    assert r(None, 64, 64, 64, qq, 64, s, None) == jf.JF_ERR_NULL
+    assert r(x, 64, 64, 64, qq, 64, P(BASE + 0x40), None) == jf.JF_ERR_ALIAS
+
+
+def test_gelu_validation_codes():
+    g = jf.lib.jf_gelu_i8
+    q, s, qo, so = P(BASE), P(BASE + 0x10000000), P(BASE + 0x20000000), P(BASE + 0x30000000)
+    assert g(q, 64, s, 64, 64, None, 64, so, None) == jf.JF_ERR_NULL
+    assert g(q, 64, s, 64, 96 + 8, qo, 64, so, None) == jf.JF_ERR_SHAPE
+    assert g(q, 64, s, 64, 64, qo, 48, so, None) == jf.JF_ERR_LD
+    assert g(q, 64, s, 64, 64, P(BASE + 0x20000008), 64, so, None) == jf.JF_ERR_ALIGN
+    assert g(q, 64, s, 64, 64, q, 64, so, None) == jf.JF_ERR_ALIAS           # in place
+    assert g(q, 64, s, 64, 64, qo, 64, s, None) == jf.JF_ERR_ALIAS
+    assert g(q, 64, s, 0, 64, qo, 64, so, None) == jf.JF_OK                  # empty
+
+
+def test_binding_refuses_host_tensors():
+    torch = pytest.importorskip("torch")
+    with pytest.raises(ValueError):
+        jf.quantize_block(torch.zeros(32, 32))

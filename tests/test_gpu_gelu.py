@@ -1,0 +1,107 @@
+"""GPU parity: jf_gelu_i8 vs the CPU oracle, and the INT8 MLP chain.
+
+Bar: output codes within 1 LSB on at most 0.01% of elements, scales within
+1e-6 relative (the observed mismatch rates are printed).  Cases: every byte
+value including -128, scales over many decades, the edge blocks of the max
+rule (zero scale, zero codes, negative-only blocks, the 0.17 threshold), the
+16384 x 16384 memory-bound workload in full, and the GPT2-medium MLP chain
+FC1 -> GELU -> FC2 at full size on sampled row strips.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import assert_requant_close, dev, host, note
+from int8_block_quantized_amd import inputs
+from int8_block_quantized_amd import jetfire as jf
+
+pytestmark = pytest.mark.gpu
+
+
+def run(q, s, what):
+    qo, so = jf.gelu_i8(dev(q), dev(s))
+    oq, os_ = oracle.gelu(q, s)
+    frac, srel = assert_requant_close(host(qo), host(so), oq, os_, what)
+    note(f"gelu {what}: code diffs {frac:.2e}, scale rel {srel:.1e}")
+    return host(qo), host(so)
+
+
+def test_all_byte_values_and_scales():
+    g = np.random.default_rng(21)
+    q = g.integers(-128, 128, size=(256, 512)).astype(np.int8)
+    s = (10.0 ** g.uniform(-6, 3, size=(8, 16))).astype(np.float32)
+    run(q, s, "random bytes")
+
+
+def test_edge_blocks():
+    g = np.random.default_rng(22)
+    q = g.integers(-127, 128, size=(64, 256)).astype(np.int8)
+    s = np.full((2, 8), 0.05, np.float32)
+    s[0, 0] = 0.0                                             # zero scale
+    q[0:32, 32:64] = 0                                        # zero codes
+    q[0:32, 64:96] = -g.integers(1, 128, size=(32, 32))       # negative codes only
+    s[0, 2] = 0.03
+    q[0:32, 96:128] = -g.integers(1, 128, size=(32, 32))      # negative-only, far tail
+    s[0, 3] = 0.2
+    q[0:32, 128:160] = -g.integers(0, 128, size=(32, 32))     # max code 1, g(s) just under 0.17
+    q[5, 130] = 1
+    s[0, 4] = 0.2785
+    q[0:32, 160:192] = -g.integers(0, 128, size=(32, 32))     # max code 1, g(s) just over 0.17
+    q[7, 161] = 1
+    s[0, 5] = 0.2788
+    q[32:64, 0:32] = -128                                     # the one byte outside the code range
+    q[32:64, 32:64] = 127                                     # constant block
+    s[1, 1] = 1e4                                             # large x: g = x
+    s[1, 2] = 1e-30                                           # tiny x
+    run(q, s, "edge blocks")
+
+
+def test_tiny_workload():
+    x = inputs.tiny_forward().make("X")
+    qx, sx = oracle.quantize(x)
+    run(qx, sx, "tiny X")
+
+
+def test_memory_bound_workload_full():
+    wl = inputs.memory_bound()
+    note("memory-bound gelu: generating")
+    x = wl.make("X")
+    q, s = jf.quantize_block(dev(x))
+    oq, os_ = oracle.quantize(x)
+    np.testing.assert_array_equal(host(q), oq)
+    np.testing.assert_array_equal(host(s), os_)
+    note("memory-bound gelu: GPU")
+    qo, so = jf.gelu_i8(q, s)
+    qh, sh = host(qo), host(so)
+    del q, s, qo, so
+    note("memory-bound gelu: oracle")
+    oqo, oso = oracle.gelu(oq, os_)
+    frac, srel = assert_requant_close(qh, sh, oqo, oso, "memory-bound")
+    note(f"memory-bound gelu: code diffs {frac:.2e}, scale rel {srel:.1e}")
+
+
+def test_mlp_chain_fc1_gelu_fc2_full_size():
+    wl = inputs.gpt2_medium_mlp()
+    x, w1, w2 = wl.make("X"), wl.make("W1"), wl.make("W2")
+    qx, sx = jf.quantize_block(dev(x))
+    qw1, sw1 = jf.quantize_block(dev(w1))
+    qw2, sw2 = jf.quantize_block(dev(w2))
+    qh, sh = jf.gemm_i8_blockscaled(qx, sx, qw1, sw1)          # FC1  8192 x 4096
+    qg, sg = jf.gelu_i8(qh, sh)                                # GELU INT8 -> INT8
+    qy, sy = jf.gemm_i8_blockscaled(qg, sg, qw2, sw2)          # FC2  8192 x 1024
+    gy, gsy = host(qy), host(sy)
+    oqx, osx = oracle.quantize(x)
+    oqw1, osw1 = oracle.quantize(w1)
+    oqw2, osw2 = oracle.quantize(w2)
+    nbN1 = 4096 // 32
+    for I in (0, 137, 255):
+        note(f"mlp chain: row strip {I}")
+        blks = [(I, J) for J in range(nbN1)]
+        hq, hs = oracle.gemm_i8_blocks(oqx, osx, oqw1, osw1, blks)
+        strip_q = np.concatenate(list(hq), axis=1)             # 32 x 4096
+        strip_s = hs.reshape(1, nbN1)
+        gq, gs = oracle.gelu(strip_q, strip_s)
+        yq, ys = oracle.gemm_i8(gq, gs, oqw2, osw2)             # 32 x 1024
+        assert_requant_close(gy[32 * I:32 * I + 32], gsy[I:I + 1], yq, ys, f"FC2 strip {I}")
+    check_other = __import__("test_gpu_gemm").check_workload_gemms
+    check_other(wl, 8)
