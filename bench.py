@@ -1,0 +1,330 @@
+"""Benchmark: block-scaled INT8 GEMM throughput of one hidden-4096 transformer
+block's linears (fwd + dgrad + wgrad) in the INT8 data flow, on one MI355X.
+
+A step is one pass of the whole hot path over one batch of 8192 tokens:
+  quantize X and the four weights (fp32 -> INT8 + 32x32 scales),
+  QKV / out-proj / FC1 forward GEMMs with on-chip requantization,
+  requantization of the (fp32) attention output before the out-projection,
+  INT8 GELU between FC1 and FC2, FC2 forward,
+  quantize the fp32 gradients entering the block (dY of FC2, dO of the
+  out-projection, dQKV of the attention), and the eight dgrad/wgrad GEMMs.
+FC1's output gradient is FC2's dgrad output (GELU backward is not part of
+the path).  Every GEMM emits INT8 codes + per-block scales.
+
+value = (sum of 2*M*N*K over the 12 GEMMs) / (wall time of one step); the
+memory-bound kernels' time is inside the step, so this is a lower bound on
+GEMM-only TOPS (also reported).  Inputs are seeded synthetic data already
+resident in HBM.  Prints one JSON line on stdout.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+INT8_PEAK_TOPS = 5000.0          # MI355X dense INT8 MFMA, published
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic_hidden4096.json")
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--cpu-seconds", type=float, default=15.0,
+                   help="target CPU time of the oracle baseline sample (0 disables it)")
+    return p.parse_args()
+
+
+class Step:
+    """Preallocated buffers and the ordered kernel list of one step."""
+
+    def __init__(self, dev):
+        import numpy as np
+        import torch
+
+        from int8_block_quantized_amd import inputs
+        from int8_block_quantized_amd import jetfire as jf
+
+        self.jf = jf
+        self.wl = inputs.hidden4096_block()
+        T = 8192
+        t0 = time.time()
+        self.host = {}
+        self.fp = {}
+        for name in ("X", "A", "Wqkv", "Wo", "W1", "W2", "dY", "dO", "dQKV"):
+            arr = self.wl.make(name)
+            self.host[name] = arr
+            self.fp[name] = torch.from_numpy(arr).to(dev)
+        log(f"inputs generated and uploaded in {time.time() - t0:.1f} s")
+
+        def i8(r, c):
+            return (torch.empty((r, c), dtype=torch.int8, device=dev),
+                    torch.empty((r // 32, c // 32), dtype=torch.float32, device=dev))
+
+        q = {}
+        for name, t in self.fp.items():
+            q[name] = i8(*t.shape)
+        for name, (r, c) in {"QKV": (T, 12288), "O": (T, 4096), "H": (T, 16384), "G": (T, 16384),
+                             "Y": (T, 4096), "dG": (T, 16384), "dW2": (16384, 4096), "dX1": (T, 4096),
+                             "dW1": (4096, 16384), "dA": (T, 4096), "dWo": (4096, 4096),
+                             "dX": (T, 4096), "dWqkv": (4096, 12288)}.items():
+            q[name] = i8(r, c)
+        self.q = q
+        Q = lambda n: q[n]
+
+        # (kind, label, args)   kinds: quant, requant, gemm, gelu
+        self.ops = [
+            ("quant", "quantize X", ("X",)),
+            ("quant", "quantize Wqkv", ("Wqkv",)),
+            ("quant", "quantize Wo", ("Wo",)),
+            ("quant", "quantize W1", ("W1",)),
+            ("quant", "quantize W2", ("W2",)),
+            ("gemm", "qkv.fwd", ("X", "Wqkv", 0, 0, "QKV")),
+            ("requant", "requant A", ("A",)),
+            ("gemm", "out.fwd", ("A", "Wo", 0, 0, "O")),
+            ("gemm", "fc1.fwd", ("X", "W1", 0, 0, "H")),
+            ("gelu", "gelu H", ("H", "G")),
+            ("gemm", "fc2.fwd", ("G", "W2", 0, 0, "Y")),
+            ("quant", "quantize dY", ("dY",)),
+            ("gemm", "fc2.dgrad", ("dY", "W2", 0, 1, "dG")),
+            ("gemm", "fc2.wgrad", ("G", "dY", 1, 0, "dW2")),
+            ("gemm", "fc1.dgrad", ("dG", "W1", 0, 1, "dX1")),
+            ("gemm", "fc1.wgrad", ("X", "dG", 1, 0, "dW1")),
+            ("quant", "quantize dO", ("dO",)),
+            ("gemm", "out.dgrad", ("dO", "Wo", 0, 1, "dA")),
+            ("gemm", "out.wgrad", ("A", "dO", 1, 0, "dWo")),
+            ("quant", "quantize dQKV", ("dQKV",)),
+            ("gemm", "qkv.dgrad", ("dQKV", "Wqkv", 0, 1, "dX")),
+            ("gemm", "qkv.wgrad", ("X", "dQKV", 1, 0, "dWqkv")),
+        ]
+        self.meta = {}
+        for kind, label, a in self.ops:
+            if kind == "gemm":
+                an, bn, ta, tb, cn = a
+                qa, qb = Q(an)[0], Q(bn)[0]
+                M = qa.shape[1] if ta else qa.shape[0]
+                K = qa.shape[0] if ta else qa.shape[1]
+                N = qb.shape[0] if tb else qb.shape[1]
+                self.meta[label] = {"kind": kind, "M": M, "N": N, "K": K, "tA": ta, "tB": tb,
+                                    "ops": 2 * M * N * K}
+            elif kind in ("quant", "requant"):
+                r, c = self.fp[a[0]].shape
+                self.meta[label] = {"kind": kind, "bytes": r * c * 4 + r * c + (r * c // 1024) * 4}
+            else:
+                r, c = Q(a[0])[0].shape
+                self.meta[label] = {"kind": kind, "bytes": 2 * r * c + 2 * (r * c // 1024) * 4}
+        self.gemm_ops = sum(m["ops"] for m in self.meta.values() if m["kind"] == "gemm")
+        assert self.gemm_ops == self.wl.gemm_ops()
+
+    def run_op(self, kind, a):
+        jf, q = self.jf, self.q
+        if kind == "quant":
+            jf.quantize_block(self.fp[a[0]], q=q[a[0]][0], s=q[a[0]][1])
+        elif kind == "requant":
+            jf.requant_block(self.fp[a[0]], q=q[a[0]][0], s=q[a[0]][1])
+        elif kind == "gemm":
+            an, bn, ta, tb, cn = a
+            jf.gemm_i8_blockscaled(q[an][0], q[an][1], q[bn][0], q[bn][1], ta, tb, out="i8",
+                                   c=q[cn][0], sc=q[cn][1])
+        elif kind == "gelu":
+            jf.gelu_i8(q[a[0]][0], q[a[0]][1], qo=q[a[1]][0], so=q[a[1]][1])
+
+    def run(self, events=None):
+        for i, (kind, label, a) in enumerate(self.ops):
+            if events is not None:
+                events[i][0].record()
+            self.run_op(kind, a)
+            if events is not None:
+                events[i][1].record()
+
+
+def kernel_name(meta):
+    """Kernel family of a step entry (one HIP kernel instantiation each)."""
+    if meta["kind"] == "gemm":
+        return f"gemm_i8bs tA={meta['tA']} tB={meta['tB']} i8-out"
+    return {"quant": "quantize_block f32", "requant": "quantize_block f32", "gelu": "gelu_i8"}[meta["kind"]]
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "jf_device.h"):
+        h.update(open(os.path.join(ROOT, "int8_block_quantized_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def cpu_baseline(step, target_s):
+    """The oracle, as it stands, on a bounded sample of the same workload."""
+    import numpy as np
+
+    import oracle
+
+    threads = oracle.get_threads()
+    wl = step.wl
+    t0 = time.time()
+    cq = {}
+
+    def codes(name):
+        # the GELU output G and FC2's dgrad output dG are pipeline
+        # intermediates; for timing, the workload's synthetic H / dH stand in
+        if name not in cq:
+            src = {"G": "H", "dG": "dH"}.get(name, name)
+            cq[name] = oracle.quantize(step.host[src] if src in step.host else wl.make(src))
+        return cq[name]
+
+    gemms = [(label, m, a) for (kind, label, a), m in
+             ((op, step.meta[op[1]]) for op in step.ops) if kind == "gemm"]
+    for label, m, a in gemms:
+        codes(a[0]), codes(a[1])
+    log(f"cpu baseline: oracle quantized operands in {time.time() - t0:.1f} s")
+
+    def sample(frac, seed=0):
+        g = np.random.default_rng(seed)
+        ops, secs = 0, 0.0
+        for label, m, a in gemms:
+            nbM, nbN = m["M"] // 32, m["N"] // 32
+            n = max(1, int(round(frac * nbM * nbN)))
+            blks = np.stack([g.integers(nbM, size=n), g.integers(nbN, size=n)], 1)
+            (qa, sa), (qb, sb) = codes(a[0]), codes(a[1])
+            t = time.perf_counter()
+            oracle.gemm_i8_blocks(qa, sa, qb, sb, blks, ta=m["tA"], tb=m["tB"])
+            secs += time.perf_counter() - t
+            ops += n * 2 * 32 * 32 * m["K"]
+        return ops, secs
+
+    ops0, s0 = sample(2e-4, seed=1)
+    frac = 2e-4 * max(1.0, target_s / max(s0, 1e-3))
+    frac = min(frac, 0.05)
+    ops, secs = sample(frac, seed=2)
+    return {"value": ops / secs / 1e12, "unit": "TOPS", "cores": threads, "kind": "oracle",
+            "sample": (f"{frac * 100:.3f}% of the output 32x32 blocks of each of the 12 GEMMs "
+                       f"(random, seeded), INT8 output, {ops / 1e9:.1f} G ops in {secs:.1f} s; "
+                       "synthetic H/dH stand in for the GELU output and FC2 dgrad output")}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the hot path has no multi-GPU part)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU (MI355X)", file=sys.stderr)
+        sys.exit(1)
+    from int8_block_quantized_amd import _build
+
+    if not os.path.exists(_build.LIB_PATH):
+        _build.build()
+    dev = torch.device("cuda:0")
+    step = Step(dev)
+
+    for _ in range(args.warmup):
+        step.run()
+    torch.cuda.synchronize()
+
+    n_ops = len(step.ops)
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n_ops)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record()
+    for k in range(args.steps):
+        step.run(ev[k])
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+
+    # per-kernel durations (ms), averaged over the timed steps
+    per = {}
+    for i, (kind, label, a) in enumerate(step.ops):
+        d = [ev[k][i][0].elapsed_time(ev[k][i][1]) for k in range(args.steps)]
+        per[label] = sum(d) / len(d)
+
+    families = {}
+    for label, m in step.meta.items():
+        f = families.setdefault(kernel_name(m), {"ms": 0.0, "launches": 0, "ops": 0, "bytes": 0})
+        f["ms"] += per[label]
+        f["launches"] += 1
+        f["ops"] += m.get("ops", 0)
+        f["bytes"] += m.get("bytes", 0)
+    dom_name, dom = max(families.items(), key=lambda kv: kv[1]["ms"])
+    if "gemm" in dom_name:
+        achieved = dom["ops"] / (dom["ms"] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "unit": "TFLOP/s", "peak": INT8_PEAK_TOPS}
+    else:
+        achieved = dom["bytes"] / (dom["ms"] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "unit": "GB/s", "peak": HBM_PEAK_GBS}
+    roof.update({"kernel": dom_name, "achieved": round(achieved, 2),
+                 "frac": round(achieved / roof["peak"], 4),
+                 "avg_launch_us": round(dom["ms"] / dom["launches"] * 1e3, 2),
+                 "launches_per_step": dom["launches"], "traffic": None})
+    if os.path.exists(TRAFFIC_FILE):
+        tr = json.load(open(TRAFFIC_FILE))
+        if tr.get("source_digest") == source_digest() and tr.get("kernel") == dom_name:
+            roof["traffic"] = tr.get("bytes_per_launch")
+
+    gemm_ms = sum(per[l] for l, m in step.meta.items() if m["kind"] == "gemm")
+    value = step.gemm_ops / (ms_step * 1e-3) / 1e12
+    kernels = {}
+    for label, m in step.meta.items():
+        e = {"us": round(per[label] * 1e3, 1)}
+        if m["kind"] == "gemm":
+            e["tops"] = round(m["ops"] / (per[label] * 1e-3) / 1e12, 1)
+        else:
+            e["gbs"] = round(m["bytes"] / (per[label] * 1e-3) / 1e9, 1)
+        kernels[label] = e
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        try:
+            cpu = cpu_baseline(step, args.cpu_seconds)
+        except Exception as exc:  # the baseline is reported, never gating
+            log(f"cpu baseline failed: {exc!r}")
+
+    out = {
+        "metric": "block-scaled INT8 GEMM TOPS (fwd+dgrad+wgrad), hidden 4096; % of INT8 MFMA peak",
+        "value": round(value, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": "hidden-4096 transformer-block linears, 8192 tokens (8x1024): "
+                               "QKV 4096->12288, out-proj 4096->4096, FC1 4096->16384, FC2 16384->4096; "
+                               "fwd+dgrad+wgrad in the INT8 data flow with quantize/requant/GELU",
+                   "tokens": 8192, "hidden": 4096, "gemms": 12, "gemm_ops_per_step": step.gemm_ops,
+                   "block": 32},
+        "frac_of_int8_peak": round(value / INT8_PEAK_TOPS, 4),
+        "gemm_only_tops": round(step.gemm_ops / (gemm_ms * 1e-3) / 1e12, 2),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+        "host_wall_s": round(wall, 3),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
