@@ -16,6 +16,10 @@ HIPCC_FLAGS = [
     "-ffp-contract=off",
     # no packed binary32 VALU instructions in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in architectural VGPRs: the per-k-block rescale reads them
+    # with VALU instructions, and an AGPR destination would cost one extra
+    # v_accvgpr_read per element
+    "-mllvm", "-amdgpu-mfma-vgpr-form=true",
 ]
 
 
