@@ -3,7 +3,7 @@
 // Every entry point validates its arguments on the host, in the order the
 // header lists the status codes, before any HIP call, then enqueues its
 // kernels on the caller's stream.  Nothing here allocates or synchronizes.
-#include "../../include/jetfire.h"
+#include "jetfire.h"
 #include "jf_launch.h"
 
 #include <stdint.h>
