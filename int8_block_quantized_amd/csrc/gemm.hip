@@ -54,6 +54,9 @@
 #ifndef JF_GEMM_KB
 #define JF_GEMM_KB 2
 #endif
+#ifndef JF_GEMM_S
+#define JF_GEMM_S 3
+#endif
 
 namespace jf {
 namespace {
@@ -62,102 +65,96 @@ typedef int v2i __attribute__((ext_vector_type(2)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) v2i lds_v2i;
+typedef __attribute__((address_space(3))) void lds_void;
 
-// Tile of a k-contiguous operand: R logical rows x BK k-bytes, LDS [row][k].
-template <int R, int BK, int NT>
-struct TileK {
-    static constexpr int P = BK + 16;                  // row pitch: conflict-free b128 reads
-    static constexpr int kBytes = R * P;
-    static constexpr int kPer = R * BK / 16 / NT;      // 16-byte pieces per thread
-    static_assert(R * BK / 16 % NT == 0, "tile must split evenly over the workgroup");
-    u32x4 reg[kPer];
+// s_waitcnt immediate that waits until at most n vector-memory operations of
+// this wave are outstanding (expcnt and lgkmcnt left at their maxima).
+constexpr int waitcnt_vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 
-    // base/ld: stored operand; row0: first logical row of the tile; nrows:
-    // logical rows of the operand; k0: first k of the stage; K: total k.
-    __device__ __forceinline__ void load(const int8_t *__restrict__ base, int64_t ld, int row0, int nrows, int k0,
-                                         int K, int tid) {
+// One operand tile of a stage, loaded straight from global memory into LDS
+// (global_load_lds_dwordx4: lane i of a wavefront writes 16 bytes at
+// LDS base + 16 i, so one instruction fills 1 KiB).  LDS rows are not
+// padded; instead the 16-byte chunks of each row are XOR-swizzled so that
+// the fragment reads below hit distinct banks.
+//   KC = true : k-contiguous operand, LDS [R rows][BK bytes], fragments by
+//               ds_read_b128 (16 consecutive k of one row per lane);
+//   KC = false: row-contiguous operand, LDS [BK k-rows][R bytes], fragments
+//               by two ds_read_b64_tr_b8 (transposing read: in each 16-lane
+//               group, lane i receives byte i of the eight 16-byte rows
+//               addressed by lane pairs (2j, 2j+1)).
+template <int R, int BK, int NW, bool KC>
+struct DTile {
+    static constexpr int kBytes = R * BK;
+    static constexpr int kInstr = kBytes / 1024;       // wavefront loads per stage
+    static constexpr int kPerWave = kInstr / NW;
+    static_assert(kInstr % NW == 0, "tile must split evenly over the wavefronts");
+    static constexpr int CPR = KC ? BK / 16 : R / 16;  // 16-byte chunks per LDS row
+    static_assert(CPR == 2 || CPR == 4 || CPR == 8 || CPR == 16, "unsupported tile width");
+
+    // Chunk swizzle of LDS row `row`.  KC: the 16 rows read by one 16-lane
+    // pass of ds_read_b128 land in 16 distinct bank groups.  !KC: the eight
+    // k-rows x two chunks read by one 32-lane pass of the transposing read do.
+    static __device__ __forceinline__ int swz(int row) {
+        if constexpr (KC) return CPR == 2 ? (row >> 3) & 1 : CPR == 4 ? (row >> 2) & 3 : (row >> 1) & 7;
+        else if constexpr (CPR == 2) return 0;
+        else if constexpr (CPR == 4) return ((row >> 2) & 1) << 1;
+        else if constexpr (CPR == 8) return ((row >> 1) & 3) << 1;
+        else return (row & 7) << 1;
+    }
+
+    // Issue this wavefront's share of the stage's loads.  base/ld: stored
+    // operand; row0: first logical row of the tile; nrows: logical rows of
+    // the operand (rows past it are clamped: their results are discarded);
+    // k0: first k of the stage (the whole stage lies inside K).
+    static __device__ __forceinline__ void load(const int8_t *__restrict__ base, int64_t ld, int row0, int nrows,
+                                                int k0, int8_t *lds_stage, int wave, int lane) {
 #pragma unroll
-        for (int p = 0; p < kPer; ++p) {
-            const int c = tid + NT * p;
-            const int r = c / (BK / 16), kc = c % (BK / 16);
-            const int grow = min(row0 + r, nrows - 1);
-            const int k = k0 + 16 * kc;
-            reg[p] = k < K ? *reinterpret_cast<const u32x4 *>(base + (int64_t)grow * ld + k) : u32x4{0, 0, 0, 0};
+        for (int j = 0; j < kPerWave; ++j) {
+            const int i = wave * kPerWave + j;
+            const int g = i * kWave + lane;
+            const int lr = g / CPR, c = (g % CPR) ^ swz(g / CPR);
+            const int8_t *src;
+            if constexpr (KC)
+                src = base + (int64_t)min(row0 + lr, nrows - 1) * ld + k0 + 16 * c;
+            else
+                src = base + (int64_t)(k0 + lr) * ld + min(row0 + 16 * c, nrows - 16);
+            __builtin_amdgcn_global_load_lds(src, (lds_void *)(lds_stage + 1024 * i), 16, 0, 0);
         }
     }
-    __device__ __forceinline__ void store(int8_t *__restrict__ lds, int tid) const {
-#pragma unroll
-        for (int p = 0; p < kPer; ++p) {
-            const int c = tid + NT * p;
-            const int r = c / (BK / 16), kc = c % (BK / 16);
-            *reinterpret_cast<u32x4 *>(lds + r * P + 16 * kc) = reg[p];
-        }
-    }
+
     // Fragment of block row `brow` (tile-local) at k-block `kk` of the stage:
     // lane -> row (lane & 31), k = 32 kk + 16 (lane >> 5) + 0..15.
     static __device__ __forceinline__ v4i frag(const int8_t *lds, int brow, int kk, int lane) {
-        return *reinterpret_cast<const v4i *>(lds + (brow * kBlock + (lane & 31)) * P + kk * kBlock +
-                                              16 * (lane >> 5));
+        if constexpr (KC) {
+            const int rr = brow * kBlock + (lane & 31), c = 2 * kk + (lane >> 5);
+            return *reinterpret_cast<const v4i *>(lds + rr * BK + 16 * (c ^ swz(rr)));
+        } else {
+            const int g = lane >> 4, m = lane & 15;
+            const int kr = kk * kBlock + 16 * (g >> 1) + (m >> 1), c = 2 * brow + (g & 1);
+            const v2i lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                (lds_v2i *)(lds + kr * R + 16 * (c ^ swz(kr)) + 8 * (m & 1)));
+            const v2i hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                (lds_v2i *)(lds + (kr + 8) * R + 16 * (c ^ swz(kr + 8)) + 8 * (m & 1)));
+            return v4i{lo.x, lo.y, hi.x, hi.y};
+        }
     }
 };
 
-// Tile of a row-contiguous operand: BK k-rows x R logical rows, LDS [k][row].
-template <int R, int BK, int NT>
-struct TileT {
-    static constexpr int P = R + 32;                   // row pitch: conflict-free tr8 reads
-    static constexpr int kBytes = BK * P;
-    static constexpr int kPer = BK * R / 16 / NT;
-    static_assert(BK * R / 16 % NT == 0, "tile must split evenly over the workgroup");
-    u32x4 reg[kPer];
-
-    __device__ __forceinline__ void load(const int8_t *__restrict__ base, int64_t ld, int row0, int nrows, int k0,
-                                         int K, int tid) {
-#pragma unroll
-        for (int p = 0; p < kPer; ++p) {
-            const int c = tid + NT * p;
-            const int k = c / (R / 16), ic = c % (R / 16);
-            const int gcol = min(row0 + 16 * ic, nrows - 16);
-            const int kr = k0 + k;
-            reg[p] = kr < K ? *reinterpret_cast<const u32x4 *>(base + (int64_t)kr * ld + gcol) : u32x4{0, 0, 0, 0};
-        }
-    }
-    __device__ __forceinline__ void store(int8_t *__restrict__ lds, int tid) const {
-#pragma unroll
-        for (int p = 0; p < kPer; ++p) {
-            const int c = tid + NT * p;
-            const int k = c / (R / 16), ic = c % (R / 16);
-            *reinterpret_cast<u32x4 *>(lds + k * P + 16 * ic) = reg[p];
-        }
-    }
-    // Same fragment as TileK::frag, gathered from the [k][row] layout: two
-    // transposing reads of 8 k-rows each.  In 16-lane group g, lane pair
-    // (2j, 2j+1) addresses k-row 16 (g/2) + j, columns 16 (g%2) .. +15.
-    static __device__ __forceinline__ v4i frag(const int8_t *lds, int brow, int kk, int lane) {
-        const int g = lane >> 4, m = lane & 15;
-        const int off = (kk * kBlock + 16 * (g >> 1) + (m >> 1)) * P + brow * kBlock + 16 * (g & 1) + 8 * (m & 1);
-        const v2i lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i *)(lds + off));
-        const v2i hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i *)(lds + off + 8 * P));
-        return v4i{lo.x, lo.y, hi.x, hi.y};
-    }
-};
-
-template <bool KC, int R, int BK, int NT>
-using TileOf = typename std::conditional<KC, TileK<R, BK, NT>, TileT<R, BK, NT>>::type;
-
-template <int WM, int WN, int GM, int GN, int KB, bool A_KC, bool B_KC, bool OUT_I8>
+template <int WM, int WN, int GM, int GN, int KB, int S, bool A_KC, bool B_KC, bool OUT_I8>
 __global__ __launch_bounds__(64 * GM * GN) void k_gemm_i8bs(
     const int8_t *__restrict__ A, int64_t lda, const float *__restrict__ sA, int64_t ldsa,
     const int8_t *__restrict__ B, int64_t ldb, const float *__restrict__ sB, int64_t ldsb,
     int M, int N, int K, void *__restrict__ Cv, int64_t ldc, float *__restrict__ sC, int tilesN) {
-    constexpr int NT = 64 * GM * GN;
+    constexpr int NW = GM * GN;
     constexpr int BM = GM * WM * kBlock, BN = GN * WN * kBlock, BK = KB * kBlock;
-    using TA = TileOf<A_KC, BM, BK, NT>;
-    using TB = TileOf<B_KC, BN, BK, NT>;
-    __shared__ __attribute__((aligned(16))) int8_t lds_a[2][TA::kBytes];
-    __shared__ __attribute__((aligned(16))) int8_t lds_b[2][TB::kBytes];
+    using TA = DTile<BM, BK, NW, A_KC>;
+    using TB = DTile<BN, BK, NW, B_KC>;
+    constexpr int kStageBytes = TA::kBytes + TB::kBytes;
+    constexpr int kLoadsPerStage = TA::kPerWave + TB::kPerWave;   // vector-memory ops per wave
+    // S-deep ring of stages; stage st lives in slot st % S.
+    __shared__ __attribute__((aligned(1024))) int8_t lds[S][kStageBytes];
 
-    const int tid = threadIdx.x;
-    const int lane = tid & (kWave - 1);
+    const int lane = threadIdx.x & (kWave - 1);
     const int wave = wave_id_uniform();
     const int wr = wave / GN, wc = wave % GN;
 
@@ -174,44 +171,48 @@ __global__ __launch_bounds__(64 * GM * GN) void k_gemm_i8bs(
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
 
-    const int nstage = (nkb + KB - 1) / KB;
-    TA ta;
-    TB tb;
-    if (nstage > 0) {
-        ta.load(A, lda, row0, M, 0, K, tid);
-        tb.load(B, ldb, col0, N, 0, K, tid);
-        ta.store(lds_a[0], tid);
-        tb.store(lds_b[0], tid);
-    }
-    __syncthreads();
+    // K is a multiple of BK (the host picks KB accordingly).
+    const int nstage = nkb / KB;
+    auto issue = [&](int st) {
+        int8_t *slot = lds[st % S];
+        TA::load(A, lda, row0, M, st * BK, slot, wave, lane);
+        TB::load(B, ldb, col0, N, st * BK, slot + TA::kBytes, wave, lane);
+    };
+#pragma unroll
+    for (int p = 0; p < S - 1; ++p)
+        if (p < nstage) issue(p);
 
     constexpr int NB = WM * WN, T = KB * NB;
     for (int st = 0; st < nstage; ++st) {
-        const int buf = st & 1;
-        const bool more = st + 1 < nstage;
-        if (more) {
-            ta.load(A, lda, row0, M, (st + 1) * BK, K, tid);
-            tb.load(B, ldb, col0, N, (st + 1) * BK, K, tid);
-        }
-        // Fragments and scale products of the whole stage.  k-blocks past K
-        // (last stage of a K that is not a multiple of BK) were zero-filled,
-        // so their partial is exactly 0 and fma(sigma, 0, acc) leaves acc
-        // unchanged (acc is never -0); their scale index is clamped in range.
+        // This wave's loads of stage st have landed once at most the loads of
+        // the stages issued after it are still in flight; the barrier then
+        // publishes every wave's part and retires all reads of slot (st-1)%S.
+        if (st + S - 2 < nstage)
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm((S - 2) * kLoadsPerStage));
+        else
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        // A bare barrier: __syncthreads() would also drain the loads of the
+        // later stages still in flight.
+        __builtin_amdgcn_s_barrier();
+        const int8_t *la = lds[st % S];
+        const int8_t *lb = la + TA::kBytes;
+
+        // Fragments and scale products of the whole stage.
         v4i af[KB][WM], bf[KB][WN];
         float sg[KB][WM][WN];
 #pragma unroll
         for (int kk = 0; kk < KB; ++kk) {
-            const int kb = min(st * KB + kk, nkb - 1);
+            const int kb = st * KB + kk;
             float sa[WM], sb[WN];
 #pragma unroll
             for (int a = 0; a < WM; ++a) {
-                af[kk][a] = TA::frag(lds_a[buf], wr * WM + a, kk, lane);
+                af[kk][a] = TA::frag(la, wr * WM + a, kk, lane);
                 const int I = min(I0 + a, nbM - 1);
                 sa[a] = A_KC ? sA[(int64_t)I * ldsa + kb] : sA[(int64_t)kb * ldsa + I];
             }
 #pragma unroll
             for (int b = 0; b < WN; ++b) {
-                bf[kk][b] = TB::frag(lds_b[buf], wc * WN + b, kk, lane);
+                bf[kk][b] = TB::frag(lb, wc * WN + b, kk, lane);
                 const int J = min(J0 + b, nbN - 1);
                 sb[b] = B_KC ? sB[(int64_t)J * ldsb + kb] : sB[(int64_t)kb * ldsb + J];
             }
@@ -220,6 +221,9 @@ __global__ __launch_bounds__(64 * GM * GN) void k_gemm_i8bs(
 #pragma unroll
                 for (int b = 0; b < WN; ++b) sg[kk][a][b] = sa[a] * sb[b];
         }
+        // Refill the slot freed by stage st-1 with stage st+S-1.
+        if (st + S - 1 < nstage) issue(st + S - 1);
+
         // Software pipeline over the stage's (k-block, output block) pairs:
         // the MFMA of pair t+1 is issued before the rescale of pair t, so the
         // matrix core works while the VALU converts and accumulates.
@@ -239,14 +243,6 @@ __global__ __launch_bounds__(64 * GM * GN) void k_gemm_i8bs(
             for (int r = 0; r < 16; ++r) acc[a][b][r] = __builtin_fmaf(sigma, (float)pc[r], acc[a][b][r]);
             if (t + 1 < T) pc = pn;
         }
-        if (more) {
-            // Fence: the next stage's LDS writes wait on its global loads, so
-            // they must not be hoisted above this stage's rescale work.
-            __builtin_amdgcn_sched_barrier(0);
-            ta.store(lds_a[buf ^ 1], tid);
-            tb.store(lds_b[buf ^ 1], tid);
-        }
-        __syncthreads();
     }
 
     // Epilogue.  Lane owns row 32I + (lane & 31); accumulator r is column
@@ -286,7 +282,7 @@ __global__ __launch_bounds__(64 * GM * GN) void k_gemm_i8bs(
         }
 }
 
-template <int WM, int WN, int GM, int GN, int KB, bool A_KC, bool B_KC, bool OUT_I8>
+template <int WM, int WN, int GM, int GN, int KB, int S, bool A_KC, bool B_KC, bool OUT_I8>
 hipError_t launch_cfg(int64_t M, int64_t N, int64_t K, const int8_t *A, int64_t lda, const float *sA,
                       const int8_t *B, int64_t ldb, const float *sB, void *C, int64_t ldc, float *sC,
                       hipStream_t stream) {
@@ -294,20 +290,32 @@ hipError_t launch_cfg(int64_t M, int64_t N, int64_t K, const int8_t *A, int64_t 
     const int64_t tilesM = (M + BM - 1) / BM, tilesN = (N + BN - 1) / BN;
     const int64_t ldsa = A_KC ? K / kBlock : M / kBlock;
     const int64_t ldsb = B_KC ? K / kBlock : N / kBlock;
-    hipLaunchKernelGGL((k_gemm_i8bs<WM, WN, GM, GN, KB, A_KC, B_KC, OUT_I8>), dim3((unsigned)(tilesM * tilesN)),
+    hipLaunchKernelGGL((k_gemm_i8bs<WM, WN, GM, GN, KB, S, A_KC, B_KC, OUT_I8>), dim3((unsigned)(tilesM * tilesN)),
                        dim3(64 * GM * GN), 0, stream, A, lda, sA, ldsa, B, ldb, sB, ldsb, (int)M, (int)N, (int)K, C,
                        ldc, sC, (int)tilesN);
     return hipGetLastError();
+}
+
+template <bool A_KC, bool B_KC, bool OUT_I8>
+hipError_t dispatch_kb(int64_t M, int64_t N, int64_t K, const int8_t *A, int64_t lda, const float *sA,
+                       const int8_t *B, int64_t ldb, const float *sB, void *C, int64_t ldc, float *sC,
+                       hipStream_t stream) {
+    constexpr int WM = JF_GEMM_WM, WN = JF_GEMM_WN, GM = JF_GEMM_GM, GN = JF_GEMM_GN;
+    constexpr int KB = JF_GEMM_KB, S = JF_GEMM_S;
+    // A stage must lie inside K: use KB k-blocks per stage when it divides
+    // K/32, else one.
+    if ((K / kBlock) % KB == 0)
+        return launch_cfg<WM, WN, GM, GN, KB, S, A_KC, B_KC, OUT_I8>(M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC,
+                                                                     stream);
+    return launch_cfg<WM, WN, GM, GN, 1, S, A_KC, B_KC, OUT_I8>(M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC, stream);
 }
 
 template <bool A_KC, bool B_KC>
 hipError_t dispatch_out(bool out_i8, int64_t M, int64_t N, int64_t K, const int8_t *A, int64_t lda,
                         const float *sA, const int8_t *B, int64_t ldb, const float *sB, void *C, int64_t ldc,
                         float *sC, hipStream_t stream) {
-    constexpr int WM = JF_GEMM_WM, WN = JF_GEMM_WN, GM = JF_GEMM_GM, GN = JF_GEMM_GN, KB = JF_GEMM_KB;
-    if (out_i8)
-        return launch_cfg<WM, WN, GM, GN, KB, A_KC, B_KC, true>(M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC, stream);
-    return launch_cfg<WM, WN, GM, GN, KB, A_KC, B_KC, false>(M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC, stream);
+    if (out_i8) return dispatch_kb<A_KC, B_KC, true>(M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC, stream);
+    return dispatch_kb<A_KC, B_KC, false>(M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC, stream);
 }
 
 }  // namespace
