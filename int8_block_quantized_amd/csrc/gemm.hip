@@ -21,21 +21,21 @@
 // columns 8g + 4h + r (g, r = 0..3, h = lane/32): that layout gives
 // 4-column stores and keeps a block's requantization inside one wavefront.
 //
-// Operand staging.  Tiles go global -> registers (16-byte loads along the
-// stored rows, so every load is coalesced) -> LDS, double-buffered:
+// Operand staging.  Tiles go straight from global memory into an S-deep
+// ring of LDS stages (global_load_lds_dwordx4; no VGPR round trip), one
+// barrier per stage, with the next stages' loads in flight:
 //   k-contiguous storage (A with transA=0, B with transB=1): LDS [row][k];
 //     fragments are one ds_read_b128 per lane (16 consecutive k);
 //   row-contiguous storage (A with transA=1, B with transB=0): LDS keeps the
 //     stored [k][row] order; fragments are read with two ds_read_b64_tr_b8
-//     (gfx950 transposing LDS read: in each 16-lane group, lane i receives
-//     byte i of the eight 16-byte rows addressed by lane pairs (2j, 2j+1)),
-//     so the transposition costs no VALU work.
+//     (gfx950 transposing LDS read), so the transposition costs no VALU work.
+//   Rows are XOR-swizzled in 16-byte chunks so fragment reads are free of
+//   bank conflicts.
 // A 32x32 block is square, so the transposed operand of the gradients keeps
 // its codes and its scale; only the scale-grid index order changes.
 //
 // Workgroup: GM x GN wavefronts; wavefront tile WM x WN output blocks; LDS
-// stages of KB k-blocks.  Row pitches are padded so fragment reads are free
-// of bank conflicts.
+// stages of KB k-blocks.
 #include "jf_device.h"
 #include "jf_launch.h"
 
@@ -158,7 +158,23 @@ __global__ __launch_bounds__(64 * GM * GN) void k_gemm_i8bs(
     const int wave = wave_id_uniform();
     const int wr = wave / GN, wc = wave % GN;
 
-    const int tm = blockIdx.x / tilesN, tn = blockIdx.x - tm * tilesN;
+    // Tile order.  Workgroups are dealt to the eight XCDs round-robin
+    // (XCD = blockIdx % 8), each with its own L2: renumber so that every XCD
+    // owns one contiguous range of tiles, and walk that range in groups of
+    // eight tile rows so neighbouring workgroups share A and B panels.
+    int tm, tn;
+    {
+        const int ntiles = gridDim.x, tilesM = ntiles / tilesN;
+        const int bid = blockIdx.x, x = bid % 8, j = bid / 8;
+        const int per = ntiles / 8, rem = ntiles % 8;
+        const int t = x * per + min(x, rem) + j;
+        constexpr int kGroup = 8;
+        const int in_group = kGroup * tilesN;
+        const int first_m = (t / in_group) * kGroup;
+        const int gsize = min(tilesM - first_m, kGroup);
+        tm = first_m + (t % in_group) % gsize;
+        tn = (t % in_group) / gsize;
+    }
     const int row0 = tm * BM, col0 = tn * BN;
     const int nbM = M / kBlock, nbN = N / kBlock, nkb = K / kBlock;
     const int I0 = row0 / kBlock + wr * WM, J0 = col0 / kBlock + wc * WN;
