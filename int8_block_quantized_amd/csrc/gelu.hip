@@ -4,24 +4,24 @@
 // and "Approach" (they too read and write INT8 with per-block scales).  The
 // erf form of GELU is used: g(x) = x * Phi(x), Phi(x) = erfc(-x/sqrt 2) / 2.
 //
-// Design (one wavefront per 32x32 block, four adjacent blocks per
-// workgroup).  Within a block every element is x = fl(s*q) for one of at
+// Design (each wavefront takes two adjacent 32x32 blocks and issues their
+// loads first).  Within a block every element is x = fl(s*q) for one of at
 // most 256 codes, so the kernel evaluates g once per code value, not once per
 // element:
 //   1. lane l evaluates g for the four byte values u = 4l..4l+3 (code
-//      u - 128): 256 evaluations per block instead of 1024.  Each is done in
-//      binary64 and rounded once to binary32, which is why per-code
-//      evaluation is affordable;
+//      u - 128): 256 evaluations per block instead of 1024, in binary32;
 //   2. the block max |g|: for x >= 0, g is increasing, and for x < 0,
 //      |g| < 0.16998; so when the largest code c_max present is positive and
-//      g(c_max) >= 0.17 the max is g(c_max), read from the owning lane.
+//      g(c_max) >= 0.17 the max is g(c_max), evaluated once in binary64.
 //      Otherwise (blocks with almost no positive mass) every element's |g| is
-//      looked up;
+//      looked up in a table evaluated in binary64;
 //   3. s' = fl(max/127); lane l turns its four g values into four output
-//      codes and packs them into one dword: the block's 256-entry code table
-//      is spread one dword per lane;
-//   4. each element's output code is one ds_bpermute from the lane that owns
-//      its table dword plus a byte select.
+//      codes (table_codes: exact against the binary64 reference, see there)
+//      and writes them as one dword of the wavefront's 256-byte code table
+//      in LDS;
+//   4. each element's output code is one byte read from that table (a
+//      256-byte table spans the 64 LDS banks once, so the reads never
+//      conflict).
 // HBM traffic is the algorithmic 2 bytes per element plus 8 bytes per block.
 #include "jf_device.h"
 #include "jf_launch.h"
@@ -31,97 +31,150 @@ namespace {
 
 // GELU of a binary32 input: x * Phi(x), Phi(x) = erfc(-x/sqrt 2) / 2 (the
 // erfc form keeps relative accuracy in the negative tail), evaluated in
-// binary64 and rounded once to binary32.
-__device__ __forceinline__ float gelu_f32(float x) {
+// binary64 and rounded once to binary32: the reference value.
+__device__ __forceinline__ float gelu_ref(float x) {
     const double xd = (double)x;
     return (float)(xd * (0.5 * erfc(-xd * 0.70710678118654752440)));
 }
 
-// Value g[u & 3] held by lane u >> 2 (u wave-uniform).
-__device__ __forceinline__ float lane_value(const float g[4], int u) {
-    const int src = u >> 2, j = u & 3;
-    const int b0 = __builtin_amdgcn_readlane(__float_as_int(g[0]), src);
-    const int b1 = __builtin_amdgcn_readlane(__float_as_int(g[1]), src);
-    const int b2 = __builtin_amdgcn_readlane(__float_as_int(g[2]), src);
-    const int b3 = __builtin_amdgcn_readlane(__float_as_int(g[3]), src);
-    return __int_as_float(j == 0 ? b0 : j == 1 ? b1 : j == 2 ? b2 : b3);
+// The same formula in binary32.  Checked against gelu_ref over every finite
+// binary32 input: relative error <= 2.92e-7 for x >= 0, absolute error
+// <= 4.47e-8 for x < 0.
+__device__ __forceinline__ float gelu_fast(float x) {
+    return x * (0.5f * erfcf(-x * 0.70710678118654752440f));
+}
+
+// Output codes of a lane's four table entries.  g holds gelu_fast values,
+// s2 = fl(m/127) with m = gelu_ref of the block's largest code, m >= 0.17.
+// Then |g/s2 - gref/s2| <= 127 * max(2.92e-7, 4.47e-8/0.17) < 3.8e-5, and
+// with the rounding of the quotients the candidate t = fl(g * fl(1/s2)) is
+// within 6e-5 of fl(gref/s2).  So rne(t) is the reference code unless t is
+// within 2^-13 of a half-integer; those entries (about 2.4e-4 of them) are
+// recomputed from gelu_ref with an IEEE division.
+__device__ __forceinline__ void table_codes(const float (&g)[4], const float (&x)[4], float s2, int (&code)[4]) {
+    const float r = 1.0f / s2;
+    float n[4];
+    bool near = false;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const float t = g[j] * r;
+        n[j] = __builtin_rintf(t);
+        near |= fabsf(fabsf(t - n[j]) - 0.5f) < 0x1p-13f;
+    }
+    if (__builtin_amdgcn_ballot_w64(near) != 0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float t = g[j] * r;
+            if (fabsf(fabsf(t - n[j]) - 0.5f) < 0x1p-13f) n[j] = __builtin_rintf(gelu_ref(x[j]) / s2);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) code[j] = (int)fminf(fmaxf(n[j], -127.0f), 127.0f);
 }
 
 __device__ __forceinline__ uint32_t bperm(uint32_t byte_addr, uint32_t v) {
     return (uint32_t)__builtin_amdgcn_ds_bpermute((int)byte_addr, (int)v);
 }
 
+constexpr int kPerWave = 2;   // blocks per wavefront
+
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+
+// Largest signed code among the 16 bytes of a lane (packed 16-bit maxima).
+__device__ __forceinline__ int max_code(const uint32_t (&wd)[4]) {
+    s16x2 m = {-128, -128};
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        const s16x2 v = __builtin_bit_cast(s16x2, wd[d]);
+        const s16x2 even = (s16x2)(v << 8) >> 8;   // bytes 0 and 2, sign-extended
+        const s16x2 odd = v >> 8;                  // bytes 1 and 3, sign-extended
+        m = __builtin_elementwise_max(m, __builtin_elementwise_max(even, odd));
+    }
+    return max((int)m.x, (int)m.y);
+}
+
 __global__ __launch_bounds__(256) void k_gelu_i8(const int8_t *__restrict__ q, int64_t ldq,
                                                  const float *__restrict__ s, int64_t nblk, int nbc,
                                                  int8_t *__restrict__ qo, int64_t ldqo,
                                                  float *__restrict__ so) {
+    // One 256-byte output-code table per wavefront, rebuilt for every block.
+    __shared__ uint32_t tables[4][kWave];
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t blk = (int64_t)blockIdx.x * 4 + wave_id_uniform();
-    if (blk >= nblk) return;
-    const int64_t bi = blk / nbc, bj = blk - bi * nbc;
+    const int wave = wave_id_uniform();
+    uint32_t *table = tables[wave];
+    const int64_t first = ((int64_t)blockIdx.x * 4 + wave) * kPerWave;
     const int row = lane >> 1, col = (lane & 1) * 16;
 
-    const u32x4 w = __builtin_nontemporal_load(
-        reinterpret_cast<const u32x4 *>(q + (bi * kBlock + row) * ldq + bj * kBlock + col));
-    const float sc = s[blk];
-    const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
-
-    int cmax = -128;
+    u32x4 w[kPerWave];
+    float sc[kPerWave];
 #pragma unroll
-    for (int d = 0; d < 4; ++d)
-#pragma unroll
-        for (int k = 0; k < 4; ++k) cmax = max(cmax, sbyte(wd[d], k));
-    cmax = __builtin_amdgcn_readfirstlane(wave_max(cmax));
-
-    // g for the four byte values owned by this lane: u = 4*lane + j, code u - 128.
-    float g[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) g[j] = gelu_f32(sc * (float)(4 * lane + j - 128));
-
-    const float gtop = lane_value(g, cmax + 128);
-    float m;
-    if (cmax > 0 && gtop >= 0.17f) {
-        m = gtop;
-    } else {
-        // Rare: the block's largest |g| may sit on a negative code.
-        m = 0.0f;
-#pragma unroll
-        for (int d = 0; d < 4; ++d)
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const uint32_t u = ((wd[d] >> (8 * k)) & 0xffu) ^ 0x80u;
-                const uint32_t g0 = bperm(u, __float_as_uint(g[0]));
-                const uint32_t g1 = bperm(u, __float_as_uint(g[1]));
-                const uint32_t g2 = bperm(u, __float_as_uint(g[2]));
-                const uint32_t g3 = bperm(u, __float_as_uint(g[3]));
-                const uint32_t sel = u & 3u;
-                const uint32_t gb = sel == 0 ? g0 : sel == 1 ? g1 : sel == 2 ? g2 : g3;
-                m = fmaxf(m, fabsf(__uint_as_float(gb)));
-            }
-        m = wave_max(m);
+    for (int i = 0; i < kPerWave; ++i) {
+        const int64_t blk = min(first + i, nblk - 1);   // tail: re-read, never stored
+        const int64_t bi = blk / nbc, bj = blk - bi * nbc;
+        w[i] = *reinterpret_cast<const u32x4 *>(q + (bi * kBlock + row) * ldq + bj * kBlock + col);
+        sc[i] = s[blk];
     }
-    const float s2 = block_scale(m);
 
-    uint32_t table = 0;
-    if (s2 != 0.0f)
-        table = pack4(quant_code(g[0], s2), quant_code(g[1], s2), quant_code(g[2], s2),
-                      quant_code(g[3], s2));
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i) {
+        const int64_t blk = first + i;
+        if (blk >= nblk) break;
+        const int64_t bi = blk / nbc, bj = blk - bi * nbc;
+        const uint32_t wd[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
+        const int cmax = wave_max_int(max_code(wd));
 
-    uint32_t od[4];
+        // g for the four byte values owned by this lane: u = 4*lane + j, code u - 128.
+        float x[4], g[4];
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
-        uint32_t o = 0;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const uint32_t u = ((wd[d] >> (8 * k)) & 0xffu) ^ 0x80u;
-            const uint32_t t = bperm(u, table);
-            o |= ((t >> ((u & 3u) * 8u)) & 0xffu) << (8 * k);
+        for (int j = 0; j < 4; ++j) {
+            x[j] = sc[i] * (float)(4 * lane + j - 128);
+            g[j] = gelu_fast(x[j]);
         }
-        od[d] = o;
+        // The scale comes from the reference value of the largest code.
+        const float gtop = gelu_ref(sc[i] * (float)cmax);
+        int code[4] = {0, 0, 0, 0};
+        float s2;
+        if (cmax > 0 && gtop >= 0.17f) {
+            s2 = block_scale(gtop);
+            table_codes(g, x, s2, code);
+        } else {
+            // Rare: the block's largest |g| may sit on a negative code; the
+            // whole table is evaluated with the reference formula.
+#pragma unroll
+            for (int j = 0; j < 4; ++j) g[j] = gelu_ref(x[j]);
+            float m = 0.0f;
+#pragma unroll
+            for (int d = 0; d < 4; ++d)
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const uint32_t u = ((wd[d] >> (8 * k)) & 0xffu) ^ 0x80u;
+                    const uint32_t g0 = bperm(u, __float_as_uint(g[0]));
+                    const uint32_t g1 = bperm(u, __float_as_uint(g[1]));
+                    const uint32_t g2 = bperm(u, __float_as_uint(g[2]));
+                    const uint32_t g3 = bperm(u, __float_as_uint(g[3]));
+                    const uint32_t sel = u & 3u;
+                    const uint32_t gb = sel == 0 ? g0 : sel == 1 ? g1 : sel == 2 ? g2 : g3;
+                    m = fmaxf(m, fabsf(__uint_as_float(gb)));
+                }
+            m = wave_max_nonneg(m);
+            s2 = block_scale(m);
+            if (s2 != 0.0f) quant_codes(g, s2, code);
+        }
+        table[lane] = pack4(code[0], code[1], code[2], code[3]);
+
+        // Each element's output code: one byte of the wavefront's table.
+        const uint8_t *tb = reinterpret_cast<const uint8_t *>(table);
+        uint32_t od[4];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            const uint32_t u = wd[d] ^ 0x80808080u;
+            od[d] = (uint32_t)tb[u & 0xffu] | ((uint32_t)tb[(u >> 8) & 0xffu] << 8) |
+                    ((uint32_t)tb[(u >> 16) & 0xffu] << 16) | ((uint32_t)tb[u >> 24] << 24);
+        }
+        *reinterpret_cast<u32x4 *>(qo + (bi * kBlock + row) * ldqo + bj * kBlock + col) =
+            u32x4{od[0], od[1], od[2], od[3]};
+        if (lane == 0) so[blk] = s2;
     }
-    __builtin_nontemporal_store(u32x4{od[0], od[1], od[2], od[3]},
-                                reinterpret_cast<u32x4 *>(qo + (bi * kBlock + row) * ldqo + bj * kBlock + col));
-    if (lane == 0) so[blk] = s2;
 }
 
 }  // namespace
@@ -130,7 +183,8 @@ hipError_t launch_gelu(const int8_t *q, int64_t ldq, const float *s, int64_t row
                        int8_t *qo, int64_t ldqo, float *so, hipStream_t stream) {
     const int64_t nbr = rows / kBlock, nbc = cols / kBlock, nblk = nbr * nbc;
     if (nblk == 0) return hipSuccess;
-    const int64_t grid = (nblk + 3) / 4;
+    const int64_t per_wg = 4 * kPerWave;
+    const int64_t grid = (nblk + per_wg - 1) / per_wg;
     hipLaunchKernelGGL(k_gelu_i8, dim3((unsigned)grid), dim3(256), 0, stream, q, ldq, s, nblk, (int)nbc,
                        qo, ldqo, so);
     return hipGetLastError();

@@ -276,17 +276,17 @@ __global__ __launch_bounds__(64 * GM * GN) void k_gemm_i8bs(
                 float m = 0.0f;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) m = fmaxf(m, fabsf(acc[a][b][r]));
-                m = wave_max(m);
+                m = wave_max_nonneg(m);
                 const float sc = block_scale(m);
+                int code[16];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) code[r] = 0;
+                if (sc != 0.0f) quant_codes(acc[a][b], sc, code);
                 int8_t *C = reinterpret_cast<int8_t *>(Cv);
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    uint32_t w = 0;
-                    if (sc != 0.0f)
-                        w = pack4(quant_code(acc[a][b][4 * g + 0], sc), quant_code(acc[a][b][4 * g + 1], sc),
-                                  quant_code(acc[a][b][4 * g + 2], sc), quant_code(acc[a][b][4 * g + 3], sc));
-                    *reinterpret_cast<uint32_t *>(C + row * ldc + col + 8 * g) = w;
-                }
+                for (int g = 0; g < 4; ++g)
+                    *reinterpret_cast<uint32_t *>(C + row * ldc + col + 8 * g) =
+                        pack4(code[4 * g], code[4 * g + 1], code[4 * g + 2], code[4 * g + 3]);
                 if (lane == 0) sC[(int64_t)I * nbN + J] = sc;
             } else {
                 float *C = reinterpret_cast<float *>(Cv);
