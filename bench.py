@@ -30,7 +30,7 @@ sys.path.insert(0, ROOT)
 
 INT8_PEAK_TOPS = 5000.0          # MI355X dense INT8 MFMA, published
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic_hidden4096.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic_hidden4096.md")
 
 
 def log(msg: str) -> None:
@@ -44,6 +44,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="target CPU time of the oracle baseline sample (0 disables it)")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="only run a plain elementwise copy (dst = src * 1) of MIB mebibytes 5 times (the "
+                        "known-size reference for the FETCH_SIZE/WRITE_SIZE counters) and exit")
     return p.parse_args()
 
 
@@ -157,6 +160,19 @@ def kernel_name(meta):
     return {"quant": "quantize_block f32", "requant": "quantize_block f32", "gelu": "gelu_i8"}[meta["kind"]]
 
 
+def read_traffic():
+    """key: value lines of the traffic summary (rocprofv3 FETCH_SIZE + WRITE_SIZE of
+    the dominant GEMM kernel, scaled by the plain-copy calibration)."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    out = {}
+    for line in open(TRAFFIC_FILE):
+        if line.startswith("- ") and ": " in line:
+            k, v = line[2:].split(": ", 1)
+            out[k.strip()] = v.strip().strip("`")
+    return out
+
+
 def source_digest() -> str:
     h = hashlib.sha256()
     for f in ("gemm.hip", "jf_device.h"):
@@ -222,6 +238,19 @@ def main():
 
     import torch
 
+    if args.copy_calibration:
+        dev = torch.device("cuda:0")
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            # a plain streaming kernel: reads and writes MIB each (copy_ of a
+            # contiguous tensor goes to the runtime's blit path instead)
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        print(f"copied {args.copy_calibration} MiB x 5", file=sys.stderr)
+        return
+
     if not torch.cuda.is_available():
         print("bench.py needs a GPU (MI355X)", file=sys.stderr)
         sys.exit(1)
@@ -275,10 +304,9 @@ def main():
                  "frac": round(achieved / roof["peak"], 4),
                  "avg_launch_us": round(dom["ms"] / dom["launches"] * 1e3, 2),
                  "launches_per_step": dom["launches"], "traffic": None})
-    if os.path.exists(TRAFFIC_FILE):
-        tr = json.load(open(TRAFFIC_FILE))
-        if tr.get("source_digest") == source_digest() and tr.get("kernel") == dom_name:
-            roof["traffic"] = tr.get("bytes_per_launch")
+    tr = read_traffic()
+    if tr and tr.get("source_digest") == source_digest() and tr.get("kernel") == dom_name:
+        roof["traffic"] = int(tr["bytes_per_launch"])
 
     gemm_ms = sum(per[l] for l, m in step.meta.items() if m["kind"] == "gemm")
     value = step.gemm_ops / (ms_step * 1e-3) / 1e12
