@@ -27,6 +27,24 @@ def sources():
     return sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")))
 
 
+TEST_PROBE_SRC = os.path.join(ROOT, "tests", "gelu_bound_check.hip")
+TEST_PROBE_BIN = os.path.join(ROOT, "tests", "gelu_bound_check")
+
+
+def build_test_probe(verbose: bool = False) -> str:
+    """Compile the exhaustive GELU error check used by the GPU tests."""
+    tmp = TEST_PROBE_BIN + ".tmp"
+    cmd = ["hipcc", "--offload-arch=gfx950", "-O3", "-ffp-contract=off",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", TEST_PROBE_SRC, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed:\n{res.stdout}\n{res.stderr}")
+    os.replace(tmp, TEST_PROBE_BIN)
+    return TEST_PROBE_BIN
+
+
 def build(verbose: bool = False) -> str:
     """Compile every HIP source into libjetfire.so (always recompiles)."""
     tmp = LIB_PATH + ".tmp"

@@ -24,25 +24,11 @@
 //      conflict).
 // HBM traffic is the algorithmic 2 bytes per element plus 8 bytes per block.
 #include "jf_device.h"
+#include "jf_gelu.h"
 #include "jf_launch.h"
 
 namespace jf {
 namespace {
-
-// GELU of a binary32 input: x * Phi(x), Phi(x) = erfc(-x/sqrt 2) / 2 (the
-// erfc form keeps relative accuracy in the negative tail), evaluated in
-// binary64 and rounded once to binary32: the reference value.
-__device__ __forceinline__ float gelu_ref(float x) {
-    const double xd = (double)x;
-    return (float)(xd * (0.5 * erfc(-xd * 0.70710678118654752440)));
-}
-
-// The same formula in binary32.  Checked against gelu_ref over every finite
-// binary32 input: relative error <= 2.92e-7 for x >= 0, absolute error
-// <= 4.47e-8 for x < 0.
-__device__ __forceinline__ float gelu_fast(float x) {
-    return x * (0.5f * erfcf(-x * 0.70710678118654752440f));
-}
 
 // Output codes of a lane's four table entries.  g holds gelu_fast values,
 // s2 = fl(m/127) with m = gelu_ref of the block's largest code, m >= 0.17.

@@ -1,0 +1,42 @@
+// Exhaustive check of the binary32 GELU used by the INT8 GELU kernel
+// (jf::gelu_fast) against its binary64 reference (jf::gelu_ref) over every
+// finite binary32 input.  Prints: max relative error for x >= 0, max
+// absolute error for x < 0, number of inputs where the two differ.
+// Test infrastructure: built by __graft_entry__.build(), run by
+// tests/test_gpu_gelu.py.
+#include <hip/hip_runtime.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../int8_block_quantized_amd/csrc/jf_gelu.h"
+
+__global__ void check(unsigned *res) {
+    const unsigned long long base = ((unsigned long long)blockIdx.x * blockDim.x + threadIdx.x) * 256ull;
+    float mrel = 0.f, mabs = 0.f;
+    unsigned diff = 0;
+    for (int i = 0; i < 256; ++i) {
+        const float x = __uint_as_float((unsigned)(base + i));
+        if (!(fabsf(x) < __builtin_inff())) continue;
+        const float gf = jf::gelu_fast(x), gd = jf::gelu_ref(x);
+        if (gf == gd) continue;
+        ++diff;
+        const float d = fabsf(gf - gd);
+        if (x >= 0.f) mrel = fmaxf(mrel, gd != 0.f ? d / fabsf(gd) : 1.f);
+        else mabs = fmaxf(mabs, d);
+    }
+    atomicMax(&res[0], __float_as_uint(mrel));
+    atomicMax(&res[1], __float_as_uint(mabs));
+    atomicAdd(&res[2], diff);
+}
+
+int main() {
+    unsigned *d = nullptr, h[3];
+    if (hipMalloc(&d, sizeof h) != hipSuccess || hipMemset(d, 0, sizeof h) != hipSuccess) return 2;
+    hipLaunchKernelGGL(check, dim3(65536), dim3(256), 0, 0, d);   // 2^32 inputs, 256 per thread
+    if (hipMemcpy(h, d, sizeof h, hipMemcpyDeviceToHost) != hipSuccess) return 3;
+    float rel, abs_;
+    memcpy(&rel, &h[0], 4);
+    memcpy(&abs_, &h[1], 4);
+    printf("%.6e %.6e %u\n", rel, abs_, h[2]);
+    return 0;
+}

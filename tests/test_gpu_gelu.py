@@ -105,3 +105,18 @@ def test_mlp_chain_fc1_gelu_fc2_full_size():
         assert_requant_close(gy[32 * I:32 * I + 32], gsy[I:I + 1], yq, ys, f"FC2 strip {I}")
     check_other = __import__("test_gpu_gemm").check_workload_gemms
     check_other(wl, 8)
+
+
+def test_binary32_gelu_error_bound_exhaustive():
+    """The kernel's tie window assumes gelu_fast is within 2.92e-7 (relative,
+    x >= 0) and 4.47e-8 (absolute, x < 0) of gelu_ref; check every finite
+    binary32 input."""
+    import os
+    import subprocess
+
+    exe = os.path.join(os.path.dirname(os.path.abspath(__file__)), "gelu_bound_check")
+    assert os.path.exists(exe), "tests/gelu_bound_check is not built (run __graft_entry__.build())"
+    out = subprocess.run([exe], capture_output=True, text=True, timeout=120, check=True).stdout.split()
+    rel, abs_err, ndiff = float(out[0]), float(out[1]), int(out[2])
+    note(f"gelu_fast vs gelu_ref: rel {rel:.3e} (x>=0), abs {abs_err:.3e} (x<0), {ndiff} inputs differ")
+    assert rel <= 2.92e-7 and abs_err <= 4.47e-8
