@@ -32,7 +32,7 @@ namespace {
 
 // Output codes of a lane's four table entries.  g holds gelu_fast values,
 // s2 = fl(m/127) with m = gelu_ref of the block's largest code, m >= 0.17.
-// Then |g/s2 - gref/s2| <= 127 * max(2.92e-7, 4.47e-8/0.17) < 3.8e-5, and
+// Then |g/s2 - gref/s2| <= 127 * max(2.93e-7, 4.48e-8/0.17) < 3.8e-5, and
 // with the rounding of the quotients the candidate t = fl(g * fl(1/s2)) is
 // within 6e-5 of fl(gref/s2).  So rne(t) is the reference code unless t is
 // within 2^-13 of a half-integer; those entries (about 2.4e-4 of them) are

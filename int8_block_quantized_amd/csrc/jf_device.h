@@ -77,10 +77,15 @@ __device__ __forceinline__ int quant_code(float x, float s) {
 // path for every value.  Results are clamped to [-127, 127].
 template <int N>
 __device__ __forceinline__ void quant_codes(const float (&x)[N], float s, int (&code)[N]) {
+    // The division paths go one value at a time (scheduling barriers between
+    // them), so their temporaries do not add to the caller's register peak.
     const float r = 1.0f / s;
     if (!(r < __builtin_inff())) {
 #pragma unroll
-        for (int e = 0; e < N; ++e) code[e] = quant_code(x[e], s);
+        for (int e = 0; e < N; ++e) {
+            code[e] = quant_code(x[e], s);
+            __builtin_amdgcn_sched_barrier(0);
+        }
         return;
     }
     float n[N];
@@ -96,6 +101,7 @@ __device__ __forceinline__ void quant_codes(const float (&x)[N], float s, int (&
         for (int e = 0; e < N; ++e) {
             const float t = x[e] * r;
             if (fabsf(fabsf(t - n[e]) - 0.5f) < 0x1p-15f) n[e] = __builtin_rintf(x[e] / s);
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 #pragma unroll

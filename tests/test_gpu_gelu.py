@@ -108,8 +108,8 @@ def test_mlp_chain_fc1_gelu_fc2_full_size():
 
 
 def test_binary32_gelu_error_bound_exhaustive():
-    """The kernel's tie window assumes gelu_fast is within 2.92e-7 (relative,
-    x >= 0) and 4.47e-8 (absolute, x < 0) of gelu_ref; check every finite
+    """The kernel's tie window assumes gelu_fast is within 2.93e-7 (relative,
+    x >= 0) and 4.48e-8 (absolute, x < 0) of gelu_ref; check every finite
     binary32 input."""
     import os
     import subprocess
@@ -119,4 +119,4 @@ def test_binary32_gelu_error_bound_exhaustive():
     out = subprocess.run([exe], capture_output=True, text=True, timeout=120, check=True).stdout.split()
     rel, abs_err, ndiff = float(out[0]), float(out[1]), int(out[2])
     note(f"gelu_fast vs gelu_ref: rel {rel:.3e} (x>=0), abs {abs_err:.3e} (x<0), {ndiff} inputs differ")
-    assert rel <= 2.92e-7 and abs_err <= 4.47e-8
+    assert rel <= 2.93e-7 and abs_err <= 4.48e-8

@@ -91,6 +91,25 @@ def test_strided_views(ta, tb):
     assert np.all(got[:, :32] == -5.0) and np.all(got[:, 32 + N:] == -5.0)
 
 
+@pytest.mark.parametrize("ta,tb", COMBOS)
+def test_wide_leading_dimension(ta, tb):
+    """Leading dimensions of 2^24 + 64 bytes: per-lane load offsets no longer
+    fit in 32 bits, which selects the kernels' 64-bit address path."""
+    M, N, K = 64, 96, 128
+    A, sA, B, sB, _ = random_operands(10, M, N, K, ta, tb)
+    ld = (1 << 24) + 64
+    note(f"wide ld: ta={ta} tb={tb}, operand buffers of {A.shape[0] * ld / 2**20:.0f} and "
+         f"{B.shape[0] * ld / 2**20:.0f} MiB")
+    bigA = torch.empty((A.shape[0], ld), dtype=torch.int8, device=DEV)
+    bigA[:, :A.shape[1]] = dev(A)
+    bigB = torch.empty((B.shape[0], ld), dtype=torch.int8, device=DEV)
+    bigB[:, ld - B.shape[1]:] = dev(B)
+    got = host(jf.gemm_i8_blockscaled(bigA[:, :A.shape[1]], dev(sA), bigB[:, ld - B.shape[1]:], dev(sB),
+                                      ta, tb, out="f32"))
+    del bigA, bigB
+    np.testing.assert_array_equal(got, oracle.gemm_f32(A, sA, B, sB, ta=ta, tb=tb))
+
+
 def test_k_zero_writes_zeros():
     M, N = 64, 96
     dummy = torch.zeros(64, dtype=torch.int8, device=DEV)
