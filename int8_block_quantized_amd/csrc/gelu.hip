@@ -4,22 +4,28 @@
 // and "Approach" (they too read and write INT8 with per-block scales).  The
 // erf form of GELU is used: g(x) = x * Phi(x), Phi(x) = erfc(-x/sqrt 2) / 2.
 //
-// Design (each wavefront takes two adjacent 32x32 blocks and issues their
-// loads first).  Within a block every element is x = fl(s*q) for one of at
-// most 256 codes, so the kernel evaluates g once per code value, not once per
-// element:
-//   1. lane l evaluates g for the four byte values u = 4l..4l+3 (code
-//      u - 128): 256 evaluations per block instead of 1024, in binary32;
-//   2. the block max |g|: for x >= 0, g is increasing, and for x < 0,
-//      |g| < 0.16998; so when the largest code c_max present is positive and
-//      g(c_max) >= 0.17 the max is g(c_max), evaluated once in binary64.
-//      Otherwise (blocks with almost no positive mass) every element's |g| is
-//      looked up in a table evaluated in binary64;
-//   3. s' = fl(max/127); lane l turns its four g values into four output
-//      codes (table_codes: exact against the binary64 reference, see there)
-//      and writes them as one dword of the wavefront's 256-byte code table
-//      in LDS;
-//   4. each element's output code is one byte read from that table (a
+// Memory mapping.  A wavefront pass covers a group of four horizontally
+// adjacent 32x32 blocks: each 16-byte load or store of the wavefront spans
+// eight whole 128-byte rows of the group, so every HBM line is read and
+// written by one instruction.  Lane l holds rows 8i + l/8 (i = 0..3), bytes
+// 16(l%8)..16(l%8)+15 of the group row: all of them inside block (l%8)/2.
+// Each wavefront makes two passes, with the loads of both issued first.
+//
+// Per block, every element is x = fl(s*q) for one of at most 256 codes, so g
+// is evaluated once per code value, not once per element:
+//   1. the block's largest code c_max: a max over the block's 16 lanes (two
+//      DPP steps and four readlanes per block);
+//   2. for x >= 0, g is increasing, and for x < 0, |g| < 0.16998; so when
+//      c_max > 0 and g(c_max) >= 0.17 the block max |g| is g(c_max),
+//      evaluated in binary64 (lanes 0..3 do the four blocks of a group at
+//      once).  Otherwise (blocks with almost no positive mass) every
+//      element's |g| is looked up in a table evaluated in binary64;
+//   3. s' = fl(max/127); lane l evaluates g for the four byte values
+//      u = 4l..4l+3 (code u - 128) in binary32 (gelu_fast, a polynomial tail
+//      approximation) and turns them into four output codes (table_codes:
+//      exact against the binary64 reference, see there), one dword of the
+//      block's 256-byte code table in LDS;
+//   4. each element's output code is one byte read from its block's table (a
 //      256-byte table spans the 64 LDS banks once, so the reads never
 //      conflict).
 // HBM traffic is the algorithmic 2 bytes per element plus 8 bytes per block.
@@ -30,39 +36,44 @@
 namespace jf {
 namespace {
 
-// Output codes of a lane's four table entries.  g holds gelu_fast values,
-// s2 = fl(m/127) with m = gelu_ref of the block's largest code, m >= 0.17.
-// Then |g/s2 - gref/s2| <= 127 * max(2.93e-7, 4.48e-8/0.17) < 3.8e-5, and
-// with the rounding of the quotients the candidate t = fl(g * fl(1/s2)) is
-// within 6e-5 of fl(gref/s2).  So rne(t) is the reference code unless t is
-// within 2^-13 of a half-integer; those entries (about 2.4e-4 of them) are
-// recomputed from gelu_ref with an IEEE division.
-__device__ __forceinline__ void table_codes(const float (&g)[4], const float (&x)[4], float s2, int (&code)[4]) {
-    const float r = 1.0f / s2;
-    float n[4];
+// gelu_ref as a call: one copy of the binary64 code instead of one per use,
+// and its constants stay out of the kernel's loop registers.
+__device__ __attribute__((noinline)) float gelu_ref_outlined(float x) { return gelu_ref(x); }
+
+// Output codes of a lane's table entries.  g holds gelu_fast values, s2 =
+// fl(m/127) with m = gelu_ref of the block's largest code, m >= 0.17, so the
+// table inputs satisfy |x| >= 0.0022 or x = 0.  In units of s2 the gap
+// between g and gref is at most 127 * 6.51e-7 = 8.3e-5 for x >= 0 and
+// 2.14e-7 * 127 / 0.17 = 1.6e-4 for x < 0; with r = rcp(s2) (hardware
+// reciprocal, within 1 ulp: at most 1.6e-5 on a quotient below 128) and the
+// roundings of t = fl(g*r) and of the reference quotient fl(gref/s2) (each
+// <= 2^-18), t is within 1.9e-4 of fl(gref/s2).  So rne(t) is the reference
+// code unless t is within 2^-12 of a half-integer; those entries (about
+// 4.9e-4 of them) are recomputed from gelu_ref with an IEEE division.
+template <int N>
+__device__ __forceinline__ void table_codes(const float (&g)[N], const float (&x)[N], float s2, int (&code)[N]) {
+    const float r = __builtin_amdgcn_rcpf(s2);
+    float n[N];
     bool near = false;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < N; ++j) {
         const float t = g[j] * r;
         n[j] = __builtin_rintf(t);
-        near |= fabsf(fabsf(t - n[j]) - 0.5f) < 0x1p-13f;
+        near |= fabsf(fabsf(t - n[j]) - 0.5f) < 0x1p-12f;
     }
     if (__builtin_amdgcn_ballot_w64(near) != 0) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < N; ++j) {
             const float t = g[j] * r;
-            if (fabsf(fabsf(t - n[j]) - 0.5f) < 0x1p-13f) n[j] = __builtin_rintf(gelu_ref(x[j]) / s2);
+            if (fabsf(fabsf(t - n[j]) - 0.5f) < 0x1p-12f) n[j] = __builtin_rintf(gelu_ref_outlined(x[j]) / s2);
         }
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) code[j] = (int)fminf(fmaxf(n[j], -127.0f), 127.0f);
+    for (int j = 0; j < N; ++j) code[j] = (int)fminf(fmaxf(n[j], -127.0f), 127.0f);
 }
 
-__device__ __forceinline__ uint32_t bperm(uint32_t byte_addr, uint32_t v) {
-    return (uint32_t)__builtin_amdgcn_ds_bpermute((int)byte_addr, (int)v);
-}
-
-constexpr int kPerWave = 2;   // blocks per wavefront
+constexpr int kGroup = 4;    // horizontally adjacent blocks per wavefront pass
+constexpr int kPasses = 2;   // passes per wavefront
 
 typedef short s16x2 __attribute__((ext_vector_type(2)));
 
@@ -79,87 +90,136 @@ __device__ __forceinline__ int max_code(const uint32_t (&wd)[4]) {
     return max((int)m.x, (int)m.y);
 }
 
+// Maximum over the 16 lanes holding one block (lanes 8r + 2b + e): DPP over
+// lane bits 0 and 3, then one readlane per row of 16.  Returns block b's
+// value (wave-uniform).
+__device__ __forceinline__ uint32_t group_reduce_rows(uint32_t v) {
+    v = max(v, dpp<kDppXor1>(v));
+    return max(v, dpp<kDppRowRor8>(v));
+}
+__device__ __forceinline__ uint32_t block_max_u(uint32_t v_rows, int b) {
+    const uint32_t a = __builtin_amdgcn_readlane(v_rows, 2 * b), c = __builtin_amdgcn_readlane(v_rows, 16 + 2 * b);
+    const uint32_t d = __builtin_amdgcn_readlane(v_rows, 32 + 2 * b), e = __builtin_amdgcn_readlane(v_rows, 48 + 2 * b);
+    return max(max(a, c), max(d, e));
+}
+__device__ __forceinline__ int block_max_i(int v_rows, int b) {
+    const int a = __builtin_amdgcn_readlane(v_rows, 2 * b), c = __builtin_amdgcn_readlane(v_rows, 16 + 2 * b);
+    const int d = __builtin_amdgcn_readlane(v_rows, 32 + 2 * b), e = __builtin_amdgcn_readlane(v_rows, 48 + 2 * b);
+    return max(max(a, c), max(d, e));
+}
+
 __global__ __launch_bounds__(256) void k_gelu_i8(const int8_t *__restrict__ q, int64_t ldq,
-                                                 const float *__restrict__ s, int64_t nblk, int nbc,
+                                                 const float *__restrict__ s, int nbc, int ngc, int64_t ngroups,
                                                  int8_t *__restrict__ qo, int64_t ldqo,
                                                  float *__restrict__ so) {
-    // One 256-byte output-code table per wavefront, rebuilt for every block.
-    __shared__ uint32_t tables[4][kWave];
+    // Per wavefront: the four blocks' output-code tables (256 bytes each)
+    // and one binary64-derived |g| table for the rare slow path.
+    __shared__ uint32_t tables[4][kGroup][kWave];
+    __shared__ float gtab[4][256];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = wave_id_uniform();
-    uint32_t *table = tables[wave];
-    const int64_t first = ((int64_t)blockIdx.x * 4 + wave) * kPerWave;
-    const int row = lane >> 1, col = (lane & 1) * 16;
+    const int r8 = lane >> 3, b = (lane & 7) >> 1, colb = (lane & 1) * 16;
+    const int64_t first = ((int64_t)blockIdx.x * 4 + wave) * kPasses;
 
-    u32x4 w[kPerWave];
-    float sc[kPerWave];
+    u32x4 w[kPasses][4];
+    float scl[kPasses];
 #pragma unroll
-    for (int i = 0; i < kPerWave; ++i) {
-        const int64_t blk = min(first + i, nblk - 1);   // tail: re-read, never stored
-        const int64_t bi = blk / nbc, bj = blk - bi * nbc;
-        w[i] = *reinterpret_cast<const u32x4 *>(q + (bi * kBlock + row) * ldq + bj * kBlock + col);
-        sc[i] = s[blk];
+    for (int p = 0; p < kPasses; ++p) {
+        const int64_t grp = min(first + p, ngroups - 1);    // tail: re-read, never stored
+        const int64_t gi = grp / ngc;
+        const int bj = min((int)(grp - gi * ngc) * kGroup + b, nbc - 1);
+        const int8_t *src = q + (gi * kBlock + r8) * ldq + (int64_t)bj * kBlock + colb;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[p][i] = *reinterpret_cast<const u32x4 *>(src + 8 * i * ldq);
+        scl[p] = s[gi * nbc + bj];
     }
 
 #pragma unroll
-    for (int i = 0; i < kPerWave; ++i) {
-        const int64_t blk = first + i;
-        if (blk >= nblk) break;
-        const int64_t bi = blk / nbc, bj = blk - bi * nbc;
-        const uint32_t wd[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
-        const int cmax = wave_max_int(max_code(wd));
+    for (int p = 0; p < kPasses; ++p) {
+        const int64_t grp = first + p;
+        if (grp >= ngroups) break;
+        const int64_t gi = grp / ngc;
+        const int gj0 = (int)(grp - gi * ngc) * kGroup;
+        const int nb = min(kGroup, nbc - gj0);             // blocks of this group
 
-        // g for the four byte values owned by this lane: u = 4*lane + j, code u - 128.
-        float x[4], g[4];
+        // Largest code of each block (per row of 16 lanes; the readlanes
+        // below finish it per block).
+        int cm = -128;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            x[j] = sc[i] * (float)(4 * lane + j - 128);
-            g[j] = gelu_fast(x[j]);
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t wd[4] = {w[p][i].x, w[p][i].y, w[p][i].z, w[p][i].w};
+            cm = max(cm, max_code(wd));
         }
-        // The scale comes from the reference value of the largest code.
-        const float gtop = gelu_ref(sc[i] * (float)cmax);
-        int code[4] = {0, 0, 0, 0};
-        float s2;
-        if (cmax > 0 && gtop >= 0.17f) {
-            s2 = block_scale(gtop);
-            table_codes(g, x, s2, code);
-        } else {
-            // Rare: the block's largest |g| may sit on a negative code; the
-            // whole table is evaluated with the reference formula.
+        const int cm_rows = (int)group_reduce_rows((uint32_t)(cm + 128)) - 128;
+        // g of each block's largest code, in binary64: lane bb does block bb.
+        float xt = 0.0f;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) g[j] = gelu_ref(x[j]);
-            float m = 0.0f;
+        for (int bb = 0; bb < kGroup; ++bb) {
+            const float scb = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(scl[p]), 2 * bb));
+            if (lane == bb) xt = scb * (float)block_max_i(cm_rows, bb);
+        }
+        const float gt_lane = gelu_ref_outlined(xt);
+
 #pragma unroll
-            for (int d = 0; d < 4; ++d)
+        for (int bb = 0; bb < kGroup; ++bb) {
+            if (bb >= nb) break;
+            const int cmax = block_max_i(cm_rows, bb);
+            const float sc = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(scl[p]), 2 * bb));
+            const float gtop = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(gt_lane), bb));
+            // g for the four byte values owned by this lane: u = 4*lane + j, code u - 128.
+            float x[4], g[4];
 #pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const uint32_t u = ((wd[d] >> (8 * k)) & 0xffu) ^ 0x80u;
-                    const uint32_t g0 = bperm(u, __float_as_uint(g[0]));
-                    const uint32_t g1 = bperm(u, __float_as_uint(g[1]));
-                    const uint32_t g2 = bperm(u, __float_as_uint(g[2]));
-                    const uint32_t g3 = bperm(u, __float_as_uint(g[3]));
-                    const uint32_t sel = u & 3u;
-                    const uint32_t gb = sel == 0 ? g0 : sel == 1 ? g1 : sel == 2 ? g2 : g3;
-                    m = fmaxf(m, fabsf(__uint_as_float(gb)));
+            for (int j = 0; j < 4; ++j) x[j] = sc * (float)(4 * lane + j - 128);
+            int code[4] = {0, 0, 0, 0};
+            float s2;
+            if (cmax > 0 && gtop >= 0.17f) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) g[j] = gelu_fast(x[j]);
+                s2 = block_scale(gtop);
+                table_codes(g, x, s2, code);
+            } else {
+                // Rare: the block's largest |g| may sit on a negative code.
+                // The whole table is evaluated with the reference formula
+                // and the block's elements look up their |g| in it.
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    g[j] = gelu_ref_outlined(x[j]);
+                    gtab[wave][4 * lane + j] = fabsf(g[j]);
                 }
-            m = wave_max_nonneg(m);
-            s2 = block_scale(m);
-            if (s2 != 0.0f) quant_codes(g, s2, code);
-        }
-        table[lane] = pack4(code[0], code[1], code[2], code[3]);
-
-        // Each element's output code: one byte of the wavefront's table.
-        const uint8_t *tb = reinterpret_cast<const uint8_t *>(table);
-        uint32_t od[4];
+                float m = 0.0f;
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
-            const uint32_t u = wd[d] ^ 0x80808080u;
-            od[d] = (uint32_t)tb[u & 0xffu] | ((uint32_t)tb[(u >> 8) & 0xffu] << 8) |
-                    ((uint32_t)tb[(u >> 16) & 0xffu] << 16) | ((uint32_t)tb[u >> 24] << 24);
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t wd[4] = {w[p][i].x, w[p][i].y, w[p][i].z, w[p][i].w};
+#pragma unroll
+                    for (int d = 0; d < 4; ++d)
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) m = fmaxf(m, gtab[wave][((wd[d] >> (8 * k)) & 0xffu) ^ 0x80u]);
+                }
+                // only the lanes of block bb count
+                s2 = block_scale(__uint_as_float(block_max_u(group_reduce_rows(__float_as_uint(m)), bb)));
+                if (s2 != 0.0f) quant_codes(g, s2, code);
+            }
+            tables[wave][bb][lane] = pack4(code[0], code[1], code[2], code[3]);
+            if (lane == 0) so[gi * nbc + gj0 + bb] = s2;
         }
-        *reinterpret_cast<u32x4 *>(qo + (bi * kBlock + row) * ldqo + bj * kBlock + col) =
-            u32x4{od[0], od[1], od[2], od[3]};
-        if (lane == 0) so[blk] = s2;
+
+        // Each element's output code: one byte of its block's table.
+        if (gj0 + b < nbc) {
+            const uint8_t *tb = reinterpret_cast<const uint8_t *>(tables[wave][b]);
+            int8_t *dst = qo + (gi * kBlock + r8) * ldqo + (int64_t)(gj0 + b) * kBlock + colb;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t wd[4] = {w[p][i].x, w[p][i].y, w[p][i].z, w[p][i].w};
+                uint32_t od[4];
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    const uint32_t u = wd[d] ^ 0x80808080u;
+                    od[d] = (uint32_t)tb[u & 0xffu] | ((uint32_t)tb[(u >> 8) & 0xffu] << 8) |
+                            ((uint32_t)tb[(u >> 16) & 0xffu] << 16) | ((uint32_t)tb[u >> 24] << 24);
+                }
+                *reinterpret_cast<u32x4 *>(dst + 8 * i * ldqo) = u32x4{od[0], od[1], od[2], od[3]};
+            }
+        }
     }
 }
 
@@ -167,12 +227,13 @@ __global__ __launch_bounds__(256) void k_gelu_i8(const int8_t *__restrict__ q, i
 
 hipError_t launch_gelu(const int8_t *q, int64_t ldq, const float *s, int64_t rows, int64_t cols,
                        int8_t *qo, int64_t ldqo, float *so, hipStream_t stream) {
-    const int64_t nbr = rows / kBlock, nbc = cols / kBlock, nblk = nbr * nbc;
-    if (nblk == 0) return hipSuccess;
-    const int64_t per_wg = 4 * kPerWave;
-    const int64_t grid = (nblk + per_wg - 1) / per_wg;
-    hipLaunchKernelGGL(k_gelu_i8, dim3((unsigned)grid), dim3(256), 0, stream, q, ldq, s, nblk, (int)nbc,
-                       qo, ldqo, so);
+    const int64_t nbr = rows / kBlock, nbc = cols / kBlock;
+    if (nbr == 0 || nbc == 0) return hipSuccess;
+    const int64_t ngc = (nbc + kGroup - 1) / kGroup, ngroups = nbr * ngc;
+    const int64_t per_wg = 4 * kPasses;
+    const int64_t grid = (ngroups + per_wg - 1) / per_wg;
+    hipLaunchKernelGGL(k_gelu_i8, dim3((unsigned)grid), dim3(256), 0, stream, q, ldq, s, (int)nbc, (int)ngc,
+                       ngroups, qo, ldqo, so);
     return hipGetLastError();
 }
 

@@ -29,6 +29,7 @@ constexpr int kDppXor1 = 0xB1;         // quad_perm [1,0,3,2]
 constexpr int kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141;  // lane i <-> 7-i within each 8
 constexpr int kDppMirror = 0x140;      // lane i <-> 15-i within each 16
+constexpr int kDppRowRor8 = 0x128;     // lane i <-> i^8 within each 16 (rotate by 8)
 
 // Wave-uniform maximum of non-negative binary32 values: for them the IEEE
 // order is the unsigned order of the bit patterns.  Rows of 16 reduce with

@@ -9,9 +9,10 @@ FC1 -> GELU -> FC2 at full size on sampled row strips.
 """
 import numpy as np
 import pytest
+import torch
 
 import oracle
-from gpu_util import assert_requant_close, dev, host, note
+from gpu_util import DEV, assert_requant_close, dev, host, note
 from int8_block_quantized_amd import inputs
 from int8_block_quantized_amd import jetfire as jf
 
@@ -54,6 +55,25 @@ def test_edge_blocks():
     s[1, 1] = 1e4                                             # large x: g = x
     s[1, 2] = 1e-30                                           # tiny x
     run(q, s, "edge blocks")
+
+
+@pytest.mark.parametrize("rows,cols", [(96, 160), (64, 96), (32, 32)])
+def test_ragged_groups_and_strided_views(rows, cols):
+    """Block-column counts that are not multiples of four (the kernel works on
+    groups of four adjacent blocks) and operands that are strided views."""
+    g = np.random.default_rng(23 + cols)
+    q = g.integers(-128, 128, size=(rows, cols)).astype(np.int8)
+    s = (10.0 ** g.uniform(-3, 1, size=(rows // 32, cols // 32))).astype(np.float32)
+    big_q = torch.zeros((rows, cols + 48), dtype=torch.int8, device=DEV)
+    big_q[:, 16:16 + cols] = dev(q)
+    big_o = torch.full((rows, cols + 64), 7, dtype=torch.int8, device=DEV)
+    so = torch.empty((rows // 32, cols // 32), dtype=torch.float32, device=DEV)
+    jf.gelu_i8(big_q[:, 16:16 + cols], dev(s), big_o[:, 32:32 + cols], so)
+    got = host(big_o)
+    oq, os_ = oracle.gelu(q, s)
+    frac, srel = assert_requant_close(got[:, 32:32 + cols], host(so), oq, os_, f"ragged {rows}x{cols}")
+    assert np.all(got[:, :32] == 7) and np.all(got[:, 32 + cols:] == 7)
+    note(f"gelu ragged {rows}x{cols}: code diffs {frac:.2e}, scale rel {srel:.1e}")
 
 
 def test_tiny_workload():
@@ -108,9 +128,9 @@ def test_mlp_chain_fc1_gelu_fc2_full_size():
 
 
 def test_binary32_gelu_error_bound_exhaustive():
-    """The kernel's tie window assumes gelu_fast is within 2.93e-7 (relative,
-    x >= 0) and 4.48e-8 (absolute, x < 0) of gelu_ref; check every finite
-    binary32 input."""
+    """The kernel's tie window assumes gelu_fast is within 6.51e-7 (relative,
+    x >= 0) and 2.14e-7 (absolute, x < 0) of gelu_ref on every binary32 input
+    with |x| >= 2^-10 or x = 0; check all of them."""
     import os
     import subprocess
 
@@ -118,5 +138,5 @@ def test_binary32_gelu_error_bound_exhaustive():
     assert os.path.exists(exe), "tests/gelu_bound_check is not built (run __graft_entry__.build())"
     out = subprocess.run([exe], capture_output=True, text=True, timeout=120, check=True).stdout.split()
     rel, abs_err, ndiff = float(out[0]), float(out[1]), int(out[2])
-    note(f"gelu_fast vs gelu_ref: rel {rel:.3e} (x>=0), abs {abs_err:.3e} (x<0), {ndiff} inputs differ")
-    assert rel <= 2.93e-7 and abs_err <= 4.48e-8
+    note(f"gelu_fast vs gelu_ref: rel {rel:.4e} (x>=0), abs {abs_err:.4e} (x<0), {ndiff} inputs differ")
+    assert rel <= 6.51e-7 and abs_err <= 2.14e-7
