@@ -21,7 +21,7 @@
 //      once).  Otherwise (blocks with almost no positive mass) every
 //      element's |g| is looked up in a table evaluated in binary64;
 //   3. s' = fl(max/127); lane l evaluates g for the four byte values
-//      u = 4l..4l+3 (code u - 128) in binary32 (gelu_fast, a polynomial tail
+//      u = 4l..4l+3 (the code whose two's-complement byte is u) in binary32 (gelu_fast, a polynomial tail
 //      approximation) and turns them into four output codes (table_codes:
 //      exact against the binary64 reference, see there), one dword of the
 //      block's 256-byte code table in LDS;
@@ -59,13 +59,13 @@ __device__ __forceinline__ void table_codes(const float (&g)[N], const float (&x
     for (int j = 0; j < N; ++j) {
         const float t = g[j] * r;
         n[j] = __builtin_rintf(t);
-        near |= fabsf(fabsf(t - n[j]) - 0.5f) < 0x1p-12f;
+        near |= fabsf(t - n[j]) > 0.5f - 0x1p-12f;   // |t - rne(t)| <= 1/2 always
     }
     if (__builtin_amdgcn_ballot_w64(near) != 0) {
 #pragma unroll
         for (int j = 0; j < N; ++j) {
             const float t = g[j] * r;
-            if (fabsf(fabsf(t - n[j]) - 0.5f) < 0x1p-12f) n[j] = __builtin_rintf(gelu_ref_outlined(x[j]) / s2);
+            if (fabsf(t - n[j]) > 0.5f - 0x1p-12f) n[j] = __builtin_rintf(gelu_ref_outlined(x[j]) / s2);
         }
     }
 #pragma unroll
@@ -76,6 +76,8 @@ constexpr int kGroup = 4;    // horizontally adjacent blocks per wavefront pass
 constexpr int kPasses = 2;   // passes per wavefront
 
 typedef short s16x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) const uint8_t lds_u8;
 
 // Largest signed code among the 16 bytes of a lane (packed 16-bit maxima).
 __device__ __forceinline__ int max_code(const uint32_t (&wd)[4]) {
@@ -114,7 +116,7 @@ __global__ __launch_bounds__(256) void k_gelu_i8(const int8_t *__restrict__ q, i
                                                  float *__restrict__ so) {
     // Per wavefront: the four blocks' output-code tables (256 bytes each)
     // and one binary64-derived |g| table for the rare slow path.
-    __shared__ uint32_t tables[4][kGroup][kWave];
+    __shared__ __attribute__((aligned(256))) uint32_t tables[4][kGroup][kWave];
     __shared__ float gtab[4][256];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = wave_id_uniform();
@@ -134,6 +136,29 @@ __global__ __launch_bounds__(256) void k_gelu_i8(const int8_t *__restrict__ q, i
         scl[p] = s[gi * nbc + bj];
     }
 
+    // Largest code of every block of both passes, and g of each block's
+    // largest code in binary64: one call, lane kGroup*p + bb evaluating
+    // block bb of pass p.
+    int cm_rows[kPasses];
+    float xt = 0.0f;
+#pragma unroll
+    for (int p = 0; p < kPasses; ++p) {
+        int cm = -128;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t wd[4] = {w[p][i].x, w[p][i].y, w[p][i].z, w[p][i].w};
+            cm = max(cm, max_code(wd));
+        }
+        // per row of 16 lanes; block_max_i finishes it per block
+        cm_rows[p] = (int)group_reduce_rows((uint32_t)(cm + 128)) - 128;
+#pragma unroll
+        for (int bb = 0; bb < kGroup; ++bb) {
+            const float scb = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(scl[p]), 2 * bb));
+            if (lane == kGroup * p + bb) xt = scb * (float)block_max_i(cm_rows[p], bb);
+        }
+    }
+    const float gt_lane = gelu_ref_outlined(xt);
+
 #pragma unroll
     for (int p = 0; p < kPasses; ++p) {
         const int64_t grp = first + p;
@@ -142,34 +167,16 @@ __global__ __launch_bounds__(256) void k_gelu_i8(const int8_t *__restrict__ q, i
         const int gj0 = (int)(grp - gi * ngc) * kGroup;
         const int nb = min(kGroup, nbc - gj0);             // blocks of this group
 
-        // Largest code of each block (per row of 16 lanes; the readlanes
-        // below finish it per block).
-        int cm = -128;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t wd[4] = {w[p][i].x, w[p][i].y, w[p][i].z, w[p][i].w};
-            cm = max(cm, max_code(wd));
-        }
-        const int cm_rows = (int)group_reduce_rows((uint32_t)(cm + 128)) - 128;
-        // g of each block's largest code, in binary64: lane bb does block bb.
-        float xt = 0.0f;
-#pragma unroll
-        for (int bb = 0; bb < kGroup; ++bb) {
-            const float scb = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(scl[p]), 2 * bb));
-            if (lane == bb) xt = scb * (float)block_max_i(cm_rows, bb);
-        }
-        const float gt_lane = gelu_ref_outlined(xt);
-
 #pragma unroll
         for (int bb = 0; bb < kGroup; ++bb) {
             if (bb >= nb) break;
-            const int cmax = block_max_i(cm_rows, bb);
+            const int cmax = block_max_i(cm_rows[p], bb);
             const float sc = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(scl[p]), 2 * bb));
-            const float gtop = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(gt_lane), bb));
-            // g for the four byte values owned by this lane: u = 4*lane + j, code u - 128.
+            const float gtop = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(gt_lane), kGroup * p + bb));
+            // g for the four byte values owned by this lane: u = 4*lane + j, code (int8_t)u.
             float x[4], g[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) x[j] = sc * (float)(4 * lane + j - 128);
+            for (int j = 0; j < 4; ++j) x[j] = sc * (float)(int8_t)(4 * lane + j);
             int code[4] = {0, 0, 0, 0};
             float s2;
             if (cmax > 0 && gtop >= 0.17f) {
@@ -193,7 +200,7 @@ __global__ __launch_bounds__(256) void k_gelu_i8(const int8_t *__restrict__ q, i
 #pragma unroll
                     for (int d = 0; d < 4; ++d)
 #pragma unroll
-                        for (int k = 0; k < 4; ++k) m = fmaxf(m, gtab[wave][((wd[d] >> (8 * k)) & 0xffu) ^ 0x80u]);
+                        for (int k = 0; k < 4; ++k) m = fmaxf(m, gtab[wave][(wd[d] >> (8 * k)) & 0xffu]);
                 }
                 // only the lanes of block bb count
                 s2 = block_scale(__uint_as_float(block_max_u(group_reduce_rows(__float_as_uint(m)), bb)));
@@ -205,7 +212,9 @@ __global__ __launch_bounds__(256) void k_gelu_i8(const int8_t *__restrict__ q, i
 
         // Each element's output code: one byte of its block's table.
         if (gj0 + b < nbc) {
-            const uint8_t *tb = reinterpret_cast<const uint8_t *>(tables[wave][b]);
+            // LDS byte address of entry u: the table is 256-byte aligned, so
+            // one byte permute puts u under the table's base address.
+            const uint32_t tbase = (uint32_t)(uintptr_t)(lds_void *)tables[wave][b];
             int8_t *dst = qo + (gi * kBlock + r8) * ldqo + (int64_t)(gj0 + b) * kBlock + colb;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -213,9 +222,13 @@ __global__ __launch_bounds__(256) void k_gelu_i8(const int8_t *__restrict__ q, i
                 uint32_t od[4];
 #pragma unroll
                 for (int d = 0; d < 4; ++d) {
-                    const uint32_t u = wd[d] ^ 0x80808080u;
-                    od[d] = (uint32_t)tb[u & 0xffu] | ((uint32_t)tb[(u >> 8) & 0xffu] << 8) |
-                            ((uint32_t)tb[(u >> 16) & 0xffu] << 16) | ((uint32_t)tb[u >> 24] << 24);
+                    uint32_t r[4];
+#pragma unroll
+                    for (int k = 0; k < 4; ++k)
+                        r[k] = *reinterpret_cast<const lds_u8 *>(
+                            (uintptr_t)__builtin_amdgcn_perm(tbase, wd[d], 0x07060500u | (uint32_t)k));
+                    od[d] = __builtin_amdgcn_perm(__builtin_amdgcn_perm(r[3], r[2], 0x0c0c0400u),
+                                                  __builtin_amdgcn_perm(r[1], r[0], 0x0c0c0400u), 0x05040100u);
                 }
                 *reinterpret_cast<u32x4 *>(dst + 8 * i * ldqo) = u32x4{od[0], od[1], od[2], od[3]};
             }
