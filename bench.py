@@ -161,8 +161,8 @@ def kernel_name(meta):
 
 
 def read_traffic():
-    """key: value lines of the traffic summary (rocprofv3 FETCH_SIZE + WRITE_SIZE of
-    the dominant GEMM kernel, scaled by the plain-copy calibration)."""
+    """key: value lines of the traffic summary (rocprofv3 FETCH_SIZE + WRITE_SIZE per
+    launch of each GEMM kernel family, scaled by the plain-copy calibration)."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     out = {}
@@ -305,8 +305,8 @@ def main():
                  "avg_launch_us": round(dom["ms"] / dom["launches"] * 1e3, 2),
                  "launches_per_step": dom["launches"], "traffic": None})
     tr = read_traffic()
-    if tr and tr.get("source_digest") == source_digest() and tr.get("kernel") == dom_name:
-        roof["traffic"] = int(tr["bytes_per_launch"])
+    if tr and tr.get("source_digest") == source_digest() and f"traffic[{dom_name}]" in tr:
+        roof["traffic"] = int(tr[f"traffic[{dom_name}]"])
 
     gemm_ms = sum(per[l] for l, m in step.meta.items() if m["kind"] == "gemm")
     value = step.gemm_ops / (ms_step * 1e-3) / 1e12

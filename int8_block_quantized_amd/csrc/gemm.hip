@@ -35,7 +35,12 @@
 // its codes and its scale; only the scale-grid index order changes.
 //
 // Workgroup: GM x GN wavefronts; wavefront tile WM x WN output blocks; LDS
-// stages of KB k-blocks.
+// stages of KB k-blocks in an S-deep ring.  Defaults: 2 x 4 wavefronts of
+// 2 x 2 blocks (a 128 x 256 tile), stages of two k-blocks, a two-deep ring,
+// each MFMA followed by its own rescale (PIPE 0), about 110 VGPRs: four
+// wavefronts per SIMD.  The rescale is VALU work (two instructions per
+// element and k-block) and the VALU issue rate of one wavefront is far below
+// the SIMD's, so occupancy, not MFMA scheduling, sets the pace.
 #include <algorithm>
 #include <type_traits>
 #include <utility>
@@ -53,17 +58,22 @@
 #define JF_GEMM_GM 2
 #endif
 #ifndef JF_GEMM_GN
-#define JF_GEMM_GN 2
+#define JF_GEMM_GN 4
+#endif
+#ifndef JF_GEMM_KB
+#define JF_GEMM_KB 2
+#endif
+#ifndef JF_GEMM_S
+#define JF_GEMM_S 2
 #endif
 #ifndef JF_GEMM_PIPE
-#define JF_GEMM_PIPE 1
+#define JF_GEMM_PIPE 0
+#endif
+#ifndef JF_GEMM_WAVES_PER_EU
+#define JF_GEMM_WAVES_PER_EU 4
 #endif
 
-#ifdef JF_GEMM_WAVES_PER_EU
 #define JF_GEMM_OCCUPANCY __attribute__((amdgpu_waves_per_eu(JF_GEMM_WAVES_PER_EU)))
-#else
-#define JF_GEMM_OCCUPANCY
-#endif
 
 namespace jf {
 namespace {
@@ -180,6 +190,25 @@ struct DTile {
         }
     }
 };
+
+// Codes of the 16 values of a lane under one non-zero block scale, with no
+// branch: the reciprocal-product candidate is replaced by the IEEE-quotient
+// code wherever it lies within 2^-15 of a half-integer (see quant_codes for
+// the bound).  Straight-line code keeps the epilogue's register demand at the
+// main loop's level; the 16 divisions cost a few percent of a tile.
+__device__ __forceinline__ void quant_codes_straight(const float (&x)[16], float s, int (&code)[16]) {
+    const float r = 1.0f / s;
+    const bool finite_r = r < __builtin_inff();
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        const float t = x[e] * r;
+        float n = __builtin_rintf(t);
+        const float qd = __builtin_rintf(x[e] / s);
+        if (!finite_r || fabsf(t - n) > 0.5f - 0x1p-15f) n = qd;
+        code[e] = (int)fminf(fmaxf(n, -127.0f), 127.0f);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
 
 template <int WM, int WN, int GM, int GN, int KB, int S, bool A_KC, bool B_KC, bool OUT_I8, bool NARROW>
 __global__ __launch_bounds__(64 * GM * GN) JF_GEMM_OCCUPANCY void k_gemm_i8bs(
@@ -398,7 +427,7 @@ __global__ __launch_bounds__(64 * GM * GN) JF_GEMM_OCCUPANCY void k_gemm_i8bs(
                 int code[16];
 #pragma unroll
                 for (int r = 0; r < 16; ++r) code[r] = 0;
-                if (sc != 0.0f) quant_codes(acc[a][b], sc, code);
+                if (sc != 0.0f) quant_codes_straight(acc[a][b], sc, code);
                 int8_t *C = reinterpret_cast<int8_t *>(Cv);
 #pragma unroll
                 for (int g = 0; g < 4; ++g)
@@ -429,11 +458,11 @@ hipError_t launch_cfg(int64_t M, int64_t N, int64_t K, const int8_t *A, int64_t 
     return hipGetLastError();
 }
 
-template <int KB, int S, bool A_KC, bool B_KC, bool OUT_I8>
+template <int GM, int GN, int KB, int S, bool A_KC, bool B_KC, bool OUT_I8>
 hipError_t dispatch_narrow(int64_t M, int64_t N, int64_t K, const int8_t *A, int64_t lda, const float *sA,
                            const int8_t *B, int64_t ldb, const float *sB, void *C, int64_t ldc, float *sC,
                            hipStream_t stream) {
-    constexpr int WM = JF_GEMM_WM, WN = JF_GEMM_WN, GM = JF_GEMM_GM, GN = JF_GEMM_GN;
+    constexpr int WM = JF_GEMM_WM, WN = JF_GEMM_WN;
     // Per-lane load offsets stay below (tile edge) * ld + tile edge; below
     // 2^31 they go in one 32-bit VGPR beside a scalar base.
     constexpr int64_t kEdge = std::max({GM * WM * kBlock, GN * WN * kBlock, KB * kBlock});
@@ -449,22 +478,14 @@ template <bool A_KC, bool B_KC, bool OUT_I8>
 hipError_t dispatch_kb(int64_t M, int64_t N, int64_t K, const int8_t *A, int64_t lda, const float *sA,
                        const int8_t *B, int64_t ldb, const float *sB, void *C, int64_t ldc, float *sC,
                        hipStream_t stream) {
-    // Stage shape.  With both operands k-contiguous, stages of two k-blocks
-    // (64-byte row segments per load) load much better than 32-byte ones
-    // (measured 0.97 vs 0.80 POP/s on the hidden-4096 activation-gradient
-    // GEMMs).  Otherwise one k-block per stage with a 4-deep ring: about 120
-    // VGPRs instead of 184, so twice the wavefronts per SIMD (measured 1.00-
-    // 1.06 vs 0.94-0.96 POP/s on the weight-gradient GEMMs).  A stage must
-    // lie inside K.
-#if defined(JF_GEMM_KB) && defined(JF_GEMM_S)
+    // Stage shape: two k-blocks per stage (64-byte row segments per load;
+    // 32-byte ones load much worse when an operand is k-contiguous) in a
+    // two-deep ring, which leaves LDS for four wavefronts per SIMD.  A stage
+    // must lie inside K; odd K/32 falls back to one k-block per stage.
     if ((K / kBlock) % JF_GEMM_KB == 0)
-        return dispatch_narrow<JF_GEMM_KB, JF_GEMM_S, A_KC, B_KC, OUT_I8>(M, N, K, A, lda, sA, B, ldb, sB, C, ldc,
-                                                                        sC, stream);
-#else
-    if (A_KC && B_KC && (K / kBlock) % 2 == 0)
-        return dispatch_narrow<2, 3, A_KC, B_KC, OUT_I8>(M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC, stream);
-#endif
-    return dispatch_narrow<1, 4, A_KC, B_KC, OUT_I8>(M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC, stream);
+        return dispatch_narrow<JF_GEMM_GM, JF_GEMM_GN, JF_GEMM_KB, JF_GEMM_S, A_KC, B_KC, OUT_I8>(
+            M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC, stream);
+    return dispatch_narrow<2, 2, 1, 4, A_KC, B_KC, OUT_I8>(M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC, stream);
 }
 
 template <bool A_KC, bool B_KC>
