@@ -109,8 +109,11 @@ template <int R, int BK, int NW, bool KC>
 struct DTile {
     static constexpr int kBytes = R * BK;
     static constexpr int kInstr = kBytes / 1024;       // wavefront loads per stage
-    static constexpr int kPerWave = kInstr / NW;
-    static_assert(kInstr % NW == 0, "tile must split evenly over the wavefronts");
+    static constexpr int kPerWave = (kInstr + NW - 1) / NW;   // wavefront w issues loads w*kPerWave + j
+    // loads issued per stage by wavefront w (fewer, or none, for the last
+    // wavefronts when the tile has fewer 1 KiB pieces than the workgroup has
+    // wavefronts times kPerWave)
+    static __device__ __forceinline__ int loads(int wave) { return max(0, min(kPerWave, kInstr - wave * kPerWave)); }
     static constexpr int CPR = KC ? BK / 16 : R / 16;  // 16-byte chunks per LDS row
     static_assert(CPR == 2 || CPR == 4 || CPR == 8 || CPR == 16, "unsupported tile width");
 
@@ -135,7 +138,7 @@ struct DTile {
                                                    Off (&off)[kPerWave]) {
 #pragma unroll
         for (int j = 0; j < kPerWave; ++j) {
-            const int g = (wave * kPerWave + j) * kWave + lane;
+            const int g = min(wave * kPerWave + j, kInstr - 1) * kWave + lane;   // unused beyond kInstr
             const int lr = g / CPR, c = (g % CPR) ^ swz(g / CPR);
             if constexpr (KC)
                 off[j] = (Off)(min(row0 + lr, nrows - 1) - row0) * (Off)ld + (Off)(16 * c);
@@ -159,9 +162,12 @@ struct DTile {
     // destination.  NARROW: per-lane offsets fit in 32 bits, so the address
     // is a scalar base plus a VGPR offset.
     template <uint32_t OFS, typename Off>
-    static __device__ __forceinline__ void issue(const int8_t *org, const Off (&off)[kPerWave], uint32_t lds_wave) {
+    static __device__ __forceinline__ void issue(const int8_t *org, const Off (&off)[kPerWave], uint32_t lds_wave,
+                                                 int wave) {
 #pragma unroll
         for (int j = 0; j < kPerWave; ++j) {
+            if (kInstr % kPerWave != 0 || kInstr < NW * kPerWave)
+                if (wave * kPerWave + j >= kInstr) break;   // uniform
             const uint32_t dst = lds_wave + OFS + 1024u * j;
             if constexpr (sizeof(Off) == 4) {
                 asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
@@ -220,7 +226,7 @@ __global__ __launch_bounds__(64 * GM * GN) JF_GEMM_OCCUPANCY void k_gemm_i8bs(
     using TA = DTile<BM, BK, NW, A_KC>;
     using TB = DTile<BN, BK, NW, B_KC>;
     constexpr int kStageBytes = TA::kBytes + TB::kBytes;
-    constexpr int kLoadsPerStage = TA::kPerWave + TB::kPerWave;   // vector-memory ops per wave
+    constexpr int kMaxLoads = TA::kPerWave + TB::kPerWave;   // vector-memory ops per wave and stage, at most
     // S-deep ring of stages; stage st lives in slot st % S.
     __shared__ __attribute__((aligned(1024))) int8_t lds[S][kStageBytes];
 
@@ -283,6 +289,7 @@ __global__ __launch_bounds__(64 * GM * GN) JF_GEMM_OCCUPANCY void k_gemm_i8bs(
     const uint32_t lds_wave = (uint32_t)(uintptr_t)(lds_void *)&lds[0][0] + 1024u * (uint32_t)wave * TA::kPerWave;
     const uint32_t lds_wave_b = (uint32_t)(uintptr_t)(lds_void *)&lds[0][0] + 1024u * (uint32_t)wave * TB::kPerWave;
     const int8_t *nextA = TA::origin(A, lda, row0, 0), *nextB = TB::origin(B, ldb, col0, 0);
+    const int nloads = TA::loads(wave) + TB::loads(wave);
     const int64_t strideA = A_KC ? BK : BK * lda, strideB = B_KC ? BK : BK * ldb;
     // Loads of the next stage into ring slot SLOT.  The LDS bases go through
     // an empty asm so the compiler recomputes each M0 value (one scalar add)
@@ -291,8 +298,8 @@ __global__ __launch_bounds__(64 * GM * GN) JF_GEMM_OCCUPANCY void k_gemm_i8bs(
         constexpr uint32_t SLOT = decltype(slot_c)::value;
         uint32_t wa = lds_wave, wb = lds_wave_b;
         asm volatile("" : "+s"(wa), "+s"(wb));
-        TA::template issue<SLOT * kStageBytes>(nextA, offA, wa);
-        TB::template issue<SLOT * kStageBytes + TA::kBytes>(nextB, offB, wb);
+        TA::template issue<SLOT * kStageBytes>(nextA, offA, wa, wave);
+        TB::template issue<SLOT * kStageBytes + TA::kBytes>(nextB, offB, wb, wave);
         nextA += strideA;
         nextB += strideB;
     };
@@ -311,10 +318,15 @@ __global__ __launch_bounds__(64 * GM * GN) JF_GEMM_OCCUPANCY void k_gemm_i8bs(
         // the stages issued after it are still in flight; the barrier then
         // publishes every wave's part and retires all reads of the slot that
         // is refilled below (read in the previous stage).
-        if (st + S - 2 < nstage)
-            asm volatile("s_waitcnt vmcnt(%0)" :: "n"((S - 2) * kLoadsPerStage) : "memory");
-        else
+        if (S > 2 && st + S - 2 < nstage) {
+            // this wavefront's own load count per stage (uniform)
+            static_for<kMaxLoads + 1>([&](auto c) {
+                if (nloads == decltype(c)::value)
+                    asm volatile("s_waitcnt vmcnt(%0)" :: "n"((S - 2) * decltype(c)::value) : "memory");
+            });
+        } else {
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
         // A bare barrier: __syncthreads() would also drain the loads of the
         // later stages still in flight.
         __builtin_amdgcn_s_barrier();
