@@ -72,6 +72,9 @@ def _load():
         lib.jfo_gelu.argtypes = [ptr, ptr, i64, i64, ptr, ptr]
         lib.jfo_gelu_value.argtypes = [ctypes.c_float]
         lib.jfo_gelu_value.restype = ctypes.c_float
+        lib.jfo_gelu_bwd.argtypes = [ptr, ptr, ptr, ptr, i64, i64, ptr, ptr]
+        lib.jfo_gelu_grad_value.argtypes = [ctypes.c_float]
+        lib.jfo_gelu_grad_value.restype = ctypes.c_float
         lib.jfo_set_threads.argtypes = [ctypes.c_int]
         lib.jfo_get_threads.restype = ctypes.c_int
         _lib = lib
@@ -213,4 +216,22 @@ def gelu(q: np.ndarray, s: np.ndarray):
     qo = np.empty((R, C), np.int8)
     so = np.empty((R // 32, C // 32), np.float32)
     _chk(_load().jfo_gelu(_p(q), _p(s), R, C, _p(qo), _p(so)), "gelu")
+    return qo, so
+
+
+def gelu_grad_value(x: float) -> float:
+    """GELU'(x) = Phi(x) + x phi(x) in binary64, rounded to binary32."""
+    return float(_load().jfo_gelu_grad_value(float(x)))
+
+
+def gelu_bwd(qdy: np.ndarray, sdy: np.ndarray, qx: np.ndarray, sx: np.ndarray):
+    """INT8 GELU backward dX = dY * GELU'(X), requantized per block: (codes, scales)."""
+    qdy, qx = _c(qdy, np.int8), _c(qx, np.int8)
+    sdy, sx = _c(sdy, np.float32), _c(sx, np.float32)
+    if qdy.shape != qx.shape or sdy.shape != sx.shape:
+        raise ValueError("dY and X must have the same shape and blocking")
+    R, C = qx.shape
+    qo = np.empty((R, C), np.int8)
+    so = np.empty((R // 32, C // 32), np.float32)
+    _chk(_load().jfo_gelu_bwd(_p(qdy), _p(sdy), _p(qx), _p(sx), R, C, _p(qo), _p(so)), "gelu_bwd")
     return qo, so

@@ -26,7 +26,10 @@
  *     accumulator becomes fmaf(sigma, (float)P, acc);
  *   - GELU: x = fl(s * q), g = x * Phi(x) with Phi(x) = erfc(-x/sqrt 2)/2
  *     evaluated in binary64 and rounded once to binary32, then the block
- *     is requantized with the same scale/code rule.
+ *     is requantized with the same scale/code rule;
+ *   - GELU backward: dy = fl(s_dy * q_dy), x = fl(s_x * q_x),
+ *     g' = Phi(x) + x phi(x) in binary64 rounded once, y = fl(dy * g'),
+ *     then the same per-block requantization.
  *
  * Build: gcc -O2 -fopenmp -ffp-contract=off (no contraction, no fast-math),
  * so every rounding below is the one written.  All matrices are dense,
@@ -306,6 +309,45 @@ int jfo_gelu(const int8_t *q, const float *s, int64_t rows, int64_t cols, int8_t
             for (int c = 0; c < JFO_B; ++c) {
                 float x = s[b] * (float)q[(bi * JFO_B + r) * cols + bj * JFO_B + c];
                 tile[r * JFO_B + c] = jfo_gelu_value(x);
+            }
+        quantize_one_block(tile, JFO_B, qo + bi * JFO_B * cols + bj * JFO_B, cols, &so[b]);
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* INT8 GELU backward (Approach: every operator of the data flow,     */
+/* the backward pass included, reads and writes INT8 with per-block   */
+/* scales).  dX = dY * GELU'(X) elementwise, both inputs INT8 + 32x32 */
+/* block scales over the same blocking, the product requantized per   */
+/* block with the same scale/code rule.                               */
+/* ------------------------------------------------------------------ */
+
+/* GELU'(x) = Phi(x) + x * phi(x), phi(x) = exp(-x^2/2) / sqrt(2 pi);
+ * binary64, rounded once to binary32. */
+float jfo_gelu_grad_value(float x)
+{
+    double xd = (double)x;
+    double cdf = 0.5 * erfc(-xd * M_SQRT1_2);
+    double pdf = exp(-0.5 * xd * xd) * 0.39894228040143267794;
+    return (float)(cdf + xd * pdf);
+}
+
+int jfo_gelu_bwd(const int8_t *qdy, const float *sdy, const int8_t *qx, const float *sx,
+                 int64_t rows, int64_t cols, int8_t *qo, float *so)
+{
+    if (!shape_ok(rows, cols)) return -1;
+    const int64_t bc = cols / JFO_B;
+#pragma omp parallel for schedule(static)
+    for (int64_t b = 0; b < (rows / JFO_B) * bc; ++b) {
+        int64_t bi = b / bc, bj = b % bc;
+        float tile[JFO_B * JFO_B];
+        for (int r = 0; r < JFO_B; ++r)
+            for (int c = 0; c < JFO_B; ++c) {
+                int64_t at = (bi * JFO_B + r) * cols + bj * JFO_B + c;
+                float dy = sdy[b] * (float)qdy[at];
+                float x = sx[b] * (float)qx[at];
+                tile[r * JFO_B + c] = dy * jfo_gelu_grad_value(x);
             }
         quantize_one_block(tile, JFO_B, qo + bi * JFO_B * cols + bj * JFO_B, cols, &so[b]);
     }
