@@ -7,9 +7,9 @@ A step is one pass of the whole hot path over one batch of 8192 tokens:
   requantization of the (fp32) attention output before the out-projection,
   INT8 GELU between FC1 and FC2, FC2 forward,
   quantize the fp32 gradients entering the block (dY of FC2, dO of the
-  out-projection, dQKV of the attention), and the eight dgrad/wgrad GEMMs.
-FC1's output gradient is FC2's dgrad output (GELU backward is not part of
-the path).  Every GEMM emits INT8 codes + per-block scales.
+  out-projection, dQKV of the attention), the eight dgrad/wgrad GEMMs, and
+  the INT8 GELU backward between FC2's dgrad output and FC1's backward GEMMs.
+Every GEMM emits INT8 codes + per-block scales.
 
 value = (sum of 2*M*N*K over the 12 GEMMs) / (wall time of one step); the
 memory-bound kernels' time is inside the step, so this is a lower bound on
@@ -81,13 +81,13 @@ class Step:
             q[name] = i8(*t.shape)
         for name, (r, c) in {"QKV": (T, 12288), "O": (T, 4096), "H": (T, 16384), "G": (T, 16384),
                              "Y": (T, 4096), "dG": (T, 16384), "dW2": (16384, 4096), "dX1": (T, 4096),
-                             "dW1": (4096, 16384), "dA": (T, 4096), "dWo": (4096, 4096),
+                             "dH": (T, 16384), "dW1": (4096, 16384), "dA": (T, 4096), "dWo": (4096, 4096),
                              "dX": (T, 4096), "dWqkv": (4096, 12288)}.items():
             q[name] = i8(r, c)
         self.q = q
         Q = lambda n: q[n]
 
-        # (kind, label, args)   kinds: quant, requant, gemm, gelu
+        # (kind, label, args)   kinds: quant, requant, gemm, gelu, gelu_bwd
         self.ops = [
             ("quant", "quantize X", ("X",)),
             ("quant", "quantize Wqkv", ("Wqkv",)),
@@ -103,8 +103,9 @@ class Step:
             ("quant", "quantize dY", ("dY",)),
             ("gemm", "fc2.dgrad", ("dY", "W2", 0, 1, "dG")),
             ("gemm", "fc2.wgrad", ("G", "dY", 1, 0, "dW2")),
-            ("gemm", "fc1.dgrad", ("dG", "W1", 0, 1, "dX1")),
-            ("gemm", "fc1.wgrad", ("X", "dG", 1, 0, "dW1")),
+            ("gelu_bwd", "gelu_bwd dG", ("dG", "H", "dH")),
+            ("gemm", "fc1.dgrad", ("dH", "W1", 0, 1, "dX1")),
+            ("gemm", "fc1.wgrad", ("X", "dH", 1, 0, "dW1")),
             ("quant", "quantize dO", ("dO",)),
             ("gemm", "out.dgrad", ("dO", "Wo", 0, 1, "dA")),
             ("gemm", "out.wgrad", ("A", "dO", 1, 0, "dWo")),
@@ -125,9 +126,12 @@ class Step:
             elif kind in ("quant", "requant"):
                 r, c = self.fp[a[0]].shape
                 self.meta[label] = {"kind": kind, "bytes": r * c * 4 + r * c + (r * c // 1024) * 4}
-            else:
+            elif kind == "gelu":
                 r, c = Q(a[0])[0].shape
                 self.meta[label] = {"kind": kind, "bytes": 2 * r * c + 2 * (r * c // 1024) * 4}
+            else:
+                r, c = Q(a[0])[0].shape
+                self.meta[label] = {"kind": kind, "bytes": 3 * r * c + 3 * (r * c // 1024) * 4}
         self.gemm_ops = sum(m["ops"] for m in self.meta.values() if m["kind"] == "gemm")
         assert self.gemm_ops == self.wl.gemm_ops()
 
@@ -143,6 +147,8 @@ class Step:
                                    c=q[cn][0], sc=q[cn][1])
         elif kind == "gelu":
             jf.gelu_i8(q[a[0]][0], q[a[0]][1], qo=q[a[1]][0], so=q[a[1]][1])
+        elif kind == "gelu_bwd":
+            jf.gelu_bwd_i8(q[a[0]][0], q[a[0]][1], q[a[1]][0], q[a[1]][1], qo=q[a[2]][0], so=q[a[2]][1])
 
     def run(self, events=None):
         for i, (kind, label, a) in enumerate(self.ops):
@@ -157,7 +163,8 @@ def kernel_name(meta):
     """Kernel family of a step entry (one HIP kernel instantiation each)."""
     if meta["kind"] == "gemm":
         return f"gemm_i8bs tA={meta['tA']} tB={meta['tB']} i8-out"
-    return {"quant": "quantize_block f32", "requant": "quantize_block f32", "gelu": "gelu_i8"}[meta["kind"]]
+    return {"quant": "quantize_block f32", "requant": "quantize_block f32", "gelu": "gelu_i8",
+            "gelu_bwd": "gelu_bwd_i8"}[meta["kind"]]
 
 
 def read_traffic():
@@ -192,10 +199,11 @@ def cpu_baseline(step, target_s):
     cq = {}
 
     def codes(name):
-        # the GELU output G and FC2's dgrad output dG are pipeline
-        # intermediates; for timing, the workload's synthetic H / dH stand in
+        # the GELU output G is a pipeline intermediate; for timing, the
+        # workload's synthetic H stands in (and its synthetic dH for the
+        # GELU-backward output)
         if name not in cq:
-            src = {"G": "H", "dG": "dH"}.get(name, name)
+            src = {"G": "H"}.get(name, name)
             cq[name] = oracle.quantize(step.host[src] if src in step.host else wl.make(src))
         return cq[name]
 
@@ -226,7 +234,7 @@ def cpu_baseline(step, target_s):
     return {"value": ops / secs / 1e12, "unit": "TOPS", "cores": threads, "kind": "oracle",
             "sample": (f"{frac * 100:.3f}% of the output 32x32 blocks of each of the 12 GEMMs "
                        f"(random, seeded), INT8 output, {ops / 1e9:.1f} G ops in {secs:.1f} s; "
-                       "synthetic H/dH stand in for the GELU output and FC2 dgrad output")}
+                       "synthetic H/dH stand in for the GELU output and the GELU-backward output")}
 
 
 def main():
@@ -341,7 +349,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": "hidden-4096 transformer-block linears, 8192 tokens (8x1024): "
                                "QKV 4096->12288, out-proj 4096->4096, FC1 4096->16384, FC2 16384->4096; "
-                               "fwd+dgrad+wgrad in the INT8 data flow with quantize/requant/GELU",
+                               "fwd+dgrad+wgrad in the INT8 data flow with quantize/requant/GELU/GELU backward",
                    "tokens": 8192, "hidden": 4096, "gemms": 12, "gemm_ops_per_step": step.gemm_ops,
                    "block": 32},
         "frac_of_int8_peak": round(value / INT8_PEAK_TOPS, 4),

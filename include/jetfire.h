@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define JF_ABI_VERSION 1
+#define JF_ABI_VERSION 2
 
 #ifndef JF_API
 #define JF_API __attribute__((visibility("default")))
@@ -138,12 +138,31 @@ JF_API jf_status jf_requant_block(const float *x, int64_t ldx, int64_t rows, int
  *   q, s    rows x cols input codes (ldq) and their scale grid
  *   qo, so  rows x cols output codes (ldqo) and their scale grid
  * Per block: x = fl(s*q); g = x * Phi(x) with Phi the standard normal CDF
- * (erf form of GELU), computed in binary32; then the per-block rule on g.
- * Matches a binary64 evaluation of g to within 1 code on a few elements in
- * 10^4 and scales to within a few ulp.  In-place operation is rejected.
+ * (erf form of GELU), evaluated in binary64 and rounded once to binary32;
+ * then the per-block rule on g.  (The kernel evaluates g per code value in
+ * binary32 and redoes in binary64 every entry whose output code it cannot
+ * decide, so codes and scales match the binary64 definition.)  In-place
+ * operation is rejected.
  */
 JF_API jf_status jf_gelu_i8(const int8_t *q, int64_t ldq, const float *s, int64_t rows, int64_t cols,
                      int8_t *qo, int64_t ldqo, float *so, hipStream_t stream);
+
+/*
+ * jf_gelu_bwd_i8 -- INT8 GELU backward: dX = dY * GELU'(X).  Pages:
+ * "Approach" (every operator of the INT8 data flow reads and writes INT8
+ * with per-block scales; the backward pass is part of that data flow).
+ *
+ *   qdy, sdy  rows x cols incoming gradient codes (lddy) and scale grid
+ *   qx, sx    rows x cols forward input codes (ldx) and scale grid, same
+ *             32x32 blocking
+ *   qo, so    rows x cols output gradient codes (ldo) and scale grid
+ * Per element: dy = fl(sdy*qdy), x = fl(sx*qx), y = fl(dy * GELU'(x)) with
+ * GELU'(x) = Phi(x) + x phi(x) evaluated in binary64 and rounded once to
+ * binary32; then the per-block rule on y.  Outputs may not overlap inputs.
+ */
+JF_API jf_status jf_gelu_bwd_i8(const int8_t *qdy, int64_t lddy, const float *sdy, const int8_t *qx, int64_t ldx,
+                                const float *sx, int64_t rows, int64_t cols, int8_t *qo, int64_t ldo, float *so,
+                                hipStream_t stream);
 
 /* Human-readable name of a status code (static storage). */
 JF_API const char *jf_status_str(jf_status status);

@@ -131,4 +131,25 @@ jf_status jf_gelu_i8(const int8_t *q, int64_t ldq, const float *s, int64_t rows,
     return hip_status(jf::launch_gelu(q, ldq, s, rows, cols, qo, ldqo, so, stream));
 }
 
+jf_status jf_gelu_bwd_i8(const int8_t *qdy, int64_t lddy, const float *sdy, const int8_t *qx, int64_t ldx,
+                         const float *sx, int64_t rows, int64_t cols, int8_t *qo, int64_t ldo, float *so,
+                         hipStream_t stream) {
+    if (missing(qdy, rows, cols) || missing(sdy, rows, cols) || missing(qx, rows, cols) ||
+        missing(sx, rows, cols) || missing(qo, rows, cols) || missing(so, rows, cols))
+        return JF_ERR_NULL;
+    if (!shape_ok(rows) || !shape_ok(cols)) return JF_ERR_SHAPE;
+    if (!ld_ok(lddy, cols, 1) || !ld_ok(ldx, cols, 1) || !ld_ok(ldo, cols, 1)) return JF_ERR_LD;
+    if (!aligned(qdy, 16) || !aligned(qx, 16) || !aligned(qo, 16) || !aligned(sdy, 4) || !aligned(sx, 4) ||
+        !aligned(so, 4))
+        return JF_ERR_ALIGN;
+    const int64_t gr = rows / kB, gc = cols / kB;
+    const Range rqo = span(qo, rows, cols, ldo, 1), rso = span(so, gr, gc, gc, 4);
+    for (Range in : {span(qdy, rows, cols, lddy, 1), span(qx, rows, cols, ldx, 1), span(sdy, gr, gc, gc, 4),
+                     span(sx, gr, gc, gc, 4)})
+        if (overlap(rqo, in) || overlap(rso, in)) return JF_ERR_ALIAS;
+    if (overlap(rqo, rso)) return JF_ERR_ALIAS;
+    if (rows == 0 || cols == 0) return JF_OK;
+    return hip_status(jf::launch_gelu_bwd(qdy, lddy, sdy, qx, ldx, sx, rows, cols, qo, ldo, so, stream));
+}
+
 }  // extern "C"

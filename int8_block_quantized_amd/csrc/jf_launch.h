@@ -19,4 +19,8 @@ hipError_t launch_gemm(int transA, int transB, int64_t M, int64_t N, int64_t K,
 hipError_t launch_gelu(const int8_t *q, int64_t ldq, const float *s, int64_t rows, int64_t cols,
                        int8_t *qo, int64_t ldqo, float *so, hipStream_t stream);
 
+hipError_t launch_gelu_bwd(const int8_t *qdy, int64_t lddy, const float *sdy, const int8_t *qx, int64_t ldx,
+                           const float *sx, int64_t rows, int64_t cols, int8_t *qo, int64_t ldo, float *so,
+                           hipStream_t stream);
+
 }  // namespace jf

@@ -27,7 +27,7 @@ JF_OUT_I8, JF_OUT_F32 = 0, 1
 
 # Every symbol include/jetfire.h declares.
 EXPORTS = ("jf_quantize_block", "jf_gemm_i8_blockscaled", "jf_requant_block", "jf_gelu_i8",
-           "jf_status_str", "jf_abi_version")
+           "jf_gelu_bwd_i8", "jf_status_str", "jf_abi_version")
 
 
 class JetfireError(RuntimeError):
@@ -50,6 +50,8 @@ def _load() -> ctypes.CDLL:
     lib.jf_gemm_i8_blockscaled.restype = cint
     lib.jf_gelu_i8.argtypes = [ptr, i64, ptr, i64, i64, ptr, i64, ptr, ptr]
     lib.jf_gelu_i8.restype = cint
+    lib.jf_gelu_bwd_i8.argtypes = [ptr, i64, ptr, ptr, i64, ptr, i64, i64, ptr, i64, ptr, ptr]
+    lib.jf_gelu_bwd_i8.restype = cint
     lib.jf_status_str.argtypes = [cint]
     lib.jf_status_str.restype = ctypes.c_char_p
     lib.jf_abi_version.restype = cint
@@ -180,4 +182,23 @@ def gelu_i8(q: torch.Tensor, s: torch.Tensor, qo: torch.Tensor | None = None,
     ldqo = _mat(qo, "qo")
     _check(lib.jf_gelu_i8(_ptr(q), ldq, _ptr(s), R, C, _ptr(qo), ldqo, _ptr(so), _stream(q.device)),
            "jf_gelu_i8")
+    return qo, so
+
+
+def gelu_bwd_i8(qdy: torch.Tensor, sdy: torch.Tensor, qx: torch.Tensor, sx: torch.Tensor,
+                qo: torch.Tensor | None = None, so: torch.Tensor | None = None):
+    """jf_gelu_bwd_i8: dX = dY * GELU'(X) on INT8 codes + scales, requantized per block."""
+    lddy, ldx = _mat(qdy, "qdy"), _mat(qx, "qx")
+    if qdy.dtype != torch.int8 or qx.dtype != torch.int8:
+        raise ValueError("qdy and qx must be int8")
+    if qdy.shape != qx.shape:
+        raise ValueError("qdy and qx must have the same shape")
+    R, C = qx.shape
+    _scales(sdy, R, C, "sdy")
+    _scales(sx, R, C, "sx")
+    qo = torch.empty((R, C), dtype=torch.int8, device=qx.device) if qo is None else qo
+    so = torch.empty((R // 32, C // 32), dtype=torch.float32, device=qx.device) if so is None else so
+    ldo = _mat(qo, "qo")
+    _check(lib.jf_gelu_bwd_i8(_ptr(qdy), lddy, _ptr(sdy), _ptr(qx), ldx, _ptr(sx), R, C, _ptr(qo), ldo, _ptr(so),
+                              _stream(qx.device)), "jf_gelu_bwd_i8")
     return qo, so

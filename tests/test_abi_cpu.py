@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert jf.abi_version() == 1
+    assert jf.abi_version() == 2
     for st in range(0, 9):
         assert jf.status_str(st) and jf.status_str(st) != "unknown status"
     assert jf.status_str(99) == "unknown status"
@@ -98,6 +98,21 @@ def test_gelu_validation_codes():
     assert g(q, 64, s, 64, 64, q, 64, so, None) == jf.JF_ERR_ALIAS           # in place
     assert g(q, 64, s, 64, 64, qo, 64, s, None) == jf.JF_ERR_ALIAS
     assert g(q, 64, s, 0, 64, qo, 64, so, None) == jf.JF_OK                  # empty
+
+
+def test_gelu_bwd_validation_codes():
+    g = jf.lib.jf_gelu_bwd_i8
+    dy, sdy, x, sx = P(BASE), P(BASE + 0x10000000), P(BASE + 0x20000000), P(BASE + 0x30000000)
+    qo, so = P(BASE + 0x40000000), P(BASE + 0x50000000)
+    assert g(dy, 64, sdy, None, 64, sx, 64, 64, qo, 64, so, None) == jf.JF_ERR_NULL
+    assert g(dy, 64, sdy, x, 64, sx, 64, 80, qo, 64, so, None) == jf.JF_ERR_SHAPE
+    assert g(dy, 64, sdy, x, 32, sx, 64, 64, qo, 64, so, None) == jf.JF_ERR_LD
+    assert g(dy, 64, sdy, x, 64, sx, 64, 64, qo, 72, so, None) == jf.JF_ERR_LD
+    assert g(dy, 64, sdy, x, 64, P(BASE + 0x30000002), 64, 64, qo, 64, so, None) == jf.JF_ERR_ALIGN
+    assert g(dy, 64, sdy, x, 64, sx, 64, 64, dy, 64, so, None) == jf.JF_ERR_ALIAS     # over dY
+    assert g(dy, 64, sdy, x, 64, sx, 64, 64, P(BASE + 0x20000100), 64, so, None) == jf.JF_ERR_ALIAS
+    assert g(dy, 64, sdy, x, 64, sx, 64, 64, qo, 64, sx, None) == jf.JF_ERR_ALIAS
+    assert g(dy, 64, sdy, x, 64, sx, 0, 64, qo, 64, so, None) == jf.JF_OK             # empty
 
 
 def test_binding_refuses_host_tensors():

@@ -1,0 +1,91 @@
+"""GPU parity: jf_gelu_bwd_i8 vs the CPU oracle.
+
+Bar: output codes within 1 LSB on at most 0.01% of elements, scales within
+1e-6 relative (the kernel evaluates the derivative per code in binary64 like
+the oracle, so no differences are expected; the observed rates are printed).
+Cases: every byte value including -128 in both inputs, scales over many
+decades, block-column counts that are not multiples of four, strided views,
+edge blocks (zero scales, x = 0, far-negative x), and the GPT2-medium MLP
+hidden gradient (8192 x 4096) in full.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import DEV, assert_requant_close, dev, host, note
+from int8_block_quantized_amd import inputs
+from int8_block_quantized_amd import jetfire as jf
+
+pytestmark = pytest.mark.gpu
+
+
+def run(qdy, sdy, qx, sx, what):
+    qo, so = jf.gelu_bwd_i8(dev(qdy), dev(sdy), dev(qx), dev(sx))
+    oq, os_ = oracle.gelu_bwd(qdy, sdy, qx, sx)
+    frac, srel = assert_requant_close(host(qo), host(so), oq, os_, what)
+    note(f"gelu_bwd {what}: code diffs {frac:.2e}, scale rel {srel:.1e}")
+
+
+@pytest.mark.parametrize("rows,cols", [(256, 512), (96, 160), (64, 96), (32, 32)])
+def test_random_bytes_and_scales(rows, cols):
+    g = np.random.default_rng(41 + cols)
+    qdy = g.integers(-128, 128, size=(rows, cols)).astype(np.int8)
+    qx = g.integers(-128, 128, size=(rows, cols)).astype(np.int8)
+    sdy = (10.0 ** g.uniform(-8, 2, size=(rows // 32, cols // 32))).astype(np.float32)
+    sx = (10.0 ** g.uniform(-4, 1, size=(rows // 32, cols // 32))).astype(np.float32)
+    run(qdy, sdy, qx, sx, f"random {rows}x{cols}")
+
+
+def test_edge_blocks():
+    g = np.random.default_rng(43)
+    qdy = g.integers(-127, 128, size=(64, 192)).astype(np.int8)
+    qx = g.integers(-127, 128, size=(64, 192)).astype(np.int8)
+    sdy = np.full((2, 6), 0.01, np.float32)
+    sx = np.full((2, 6), 0.05, np.float32)
+    sdy[0, 0] = 0.0                                   # zero gradient scale
+    sx[0, 1] = 0.0                                    # x = 0: derivative 1/2
+    qx[0:32, 64:96] = -g.integers(100, 128, size=(32, 32))
+    sx[0, 2] = 0.2                                    # far-negative x: tiny derivative
+    qdy[0:32, 96:128] = 0                             # zero gradient codes
+    qx[32:64, 0:32] = -128                            # the byte outside the code range
+    qdy[32:64, 32:64] = -128
+    sx[1, 2] = 1e4                                    # large x: derivative 1
+    sdy[1, 3] = 1e-30                                 # tiny gradients
+    run(qdy, sdy, qx, sx, "edge blocks")
+
+
+def test_strided_views():
+    g = np.random.default_rng(44)
+    rows, cols = 64, 160
+    qdy = g.integers(-128, 128, size=(rows, cols)).astype(np.int8)
+    qx = g.integers(-128, 128, size=(rows, cols)).astype(np.int8)
+    sdy = (10.0 ** g.uniform(-4, 0, size=(2, 5))).astype(np.float32)
+    sx = (10.0 ** g.uniform(-3, 0, size=(2, 5))).astype(np.float32)
+    bdy = torch.zeros((rows, cols + 32), dtype=torch.int8, device=DEV)
+    bdy[:, 32:] = dev(qdy)
+    bx = torch.zeros((rows, cols + 64), dtype=torch.int8, device=DEV)
+    bx[:, 16:16 + cols] = dev(qx)
+    bo = torch.full((rows, cols + 48), 5, dtype=torch.int8, device=DEV)
+    so = torch.empty((2, 5), dtype=torch.float32, device=DEV)
+    jf.gelu_bwd_i8(bdy[:, 32:], dev(sdy), bx[:, 16:16 + cols], dev(sx), bo[:, 16:16 + cols], so)
+    got = host(bo)
+    oq, os_ = oracle.gelu_bwd(qdy, sdy, qx, sx)
+    frac, srel = assert_requant_close(got[:, 16:16 + cols], host(so), oq, os_, "strided")
+    assert np.all(got[:, :16] == 5) and np.all(got[:, 16 + cols:] == 5)
+
+
+def test_mlp_hidden_gradient_full_size():
+    """GPT2-medium MLP: the FC1 output H (8192 x 4096) and a gradient of the
+    same shape, both quantized from the workload's synthetic tensors."""
+    wl = inputs.gpt2_medium_mlp()
+    h, dy = wl.make("H"), wl.make("dY1")
+    qh, sh = jf.quantize_block(dev(h))
+    qd, sd = jf.quantize_block(dev(dy))
+    note("gelu_bwd mlp: GPU")
+    qo, so = jf.gelu_bwd_i8(qd, sd, qh, sh)
+    gq, gs = host(qo), host(so)
+    note("gelu_bwd mlp: oracle")
+    oq, os_ = oracle.gelu_bwd(host(qd), host(sd), host(qh), host(sh))
+    frac, srel = assert_requant_close(gq, gs, oq, os_, "mlp 8192x4096")
+    note(f"gelu_bwd mlp: code diffs {frac:.2e}, scale rel {srel:.1e}")
