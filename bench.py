@@ -44,6 +44,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="target CPU time of the oracle baseline sample (0 disables it)")
+    p.add_argument("--bf16-steps", type=int, default=5,
+                   help="steps of the bf16 reference (the same 12 GEMMs with torch.mm in bfloat16; 0 skips it)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run a plain elementwise copy (dst = src * 1) of MIB mebibytes 5 times (the "
                         "known-size reference for the FETCH_SIZE/WRITE_SIZE counters) and exit")
@@ -237,6 +239,44 @@ def cpu_baseline(step, target_s):
                        "synthetic H/dH stand in for the GELU output and the GELU-backward output")}
 
 
+def bf16_reference(step, steps):
+    """The same 12 GEMM shapes as plain bfloat16 GEMMs (torch.mm, i.e. the
+    vendor BLAS), for the INT8-vs-bf16 comparison of the linear layers.
+    Operands are laid out beforehand (no transposed views), outputs are bf16,
+    inputs random N(0,1); GEMMs only, nothing else of the step."""
+    import torch
+
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    mats = []
+    for kind, label, a in step.ops:
+        if kind != "gemm":
+            continue
+        m = step.meta[label]
+        A = torch.randn((m["M"], m["K"]), device=dev, generator=g).to(torch.bfloat16)
+        B = torch.randn((m["K"], m["N"]), device=dev, generator=g).to(torch.bfloat16)
+        C = torch.empty((m["M"], m["N"]), device=dev, dtype=torch.bfloat16)
+        mats.append((A, B, C))
+
+    def run():
+        for A, B, C in mats:
+            torch.mm(A, B, out=C)
+
+    run()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        run()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    del mats
+    torch.cuda.empty_cache()
+    return ms
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -327,6 +367,14 @@ def main():
             e["gbs"] = round(m["bytes"] / (per[label] * 1e-3) / 1e9, 1)
         kernels[label] = e
 
+    bf16 = None
+    if args.bf16_steps > 0:
+        bms = bf16_reference(step, args.bf16_steps)
+        bf16 = {"ms_per_step": round(bms, 4), "tflops": round(step.gemm_ops / (bms * 1e-3) / 1e12, 2),
+                "int8_gemm_speedup": round(bms / gemm_ms, 3),
+                "what": "the 12 GEMM shapes as torch.mm in bfloat16 (vendor BLAS), operands pre-laid-out, "
+                        "bf16 outputs; compared with the INT8 GEMMs' time in the step"}
+
     cpu = None
     if args.cpu_seconds > 0:
         try:
@@ -356,6 +404,7 @@ def main():
         "gemm_only_tops": round(step.gemm_ops / (gemm_ms * 1e-3) / 1e12, 2),
         "roofline": roof,
         "cpu_baseline": cpu,
+        "bf16_reference": bf16,
         "kernels": kernels,
         "host_wall_s": round(wall, 3),
     }

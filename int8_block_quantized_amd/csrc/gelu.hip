@@ -20,11 +20,12 @@
 //      evaluated in binary64 (lanes 0..3 do the four blocks of a group at
 //      once).  Otherwise (blocks with almost no positive mass) every
 //      element's |g| is looked up in a table evaluated in binary64;
-//   3. s' = fl(max/127); lane l evaluates g for the four byte values
-//      u = 4l..4l+3 (the code whose two's-complement byte is u) in binary32 (gelu_fast, a polynomial tail
-//      approximation) and turns them into four output codes (table_codes:
-//      exact against the binary64 reference, see there), one dword of the
-//      block's 256-byte code table in LDS;
+//   3. s' = fl(max/127); lane l evaluates g for the codes +-(2l+1) and
+//      +-(2l+2) in binary32 (gelu_fast's polynomial tail approximation: one
+//      tail value per pair, as g(x) = x - xQ(x) and g(-x) = -xQ(x)) and turns
+//      them into output codes (table_codes: exact against the binary64
+//      reference, see there), bytes of the block's 256-entry code table in
+//      LDS, indexed by the code's raw byte;
 //   4. each element's output code is one byte read from its block's table (a
 //      256-byte table spans the 64 LDS banks once, so the reads never
 //      conflict).
@@ -173,18 +174,37 @@ __global__ __launch_bounds__(256) void k_gelu_i8(const int8_t *__restrict__ q, i
             const int cmax = block_max_i(cm_rows[p], bb);
             const float sc = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(scl[p]), 2 * bb));
             const float gtop = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(gt_lane), kGroup * p + bb));
-            // g for the four byte values owned by this lane: u = 4*lane + j, code (int8_t)u.
             float x[4], g[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) x[j] = sc * (float)(int8_t)(4 * lane + j);
             int code[4] = {0, 0, 0, 0};
             float s2;
             if (cmax > 0 && gtop >= 0.17f) {
+                // Lane l takes the code pairs +-p, p = 2l+1 and 2l+2: one tail
+                // value Q serves g(x) = x - xQ and g(-x) = -xQ (the same
+                // arithmetic as gelu_fast on each); code 0 gives 0.  The
+                // pair p = 128 only has its negative code.
 #pragma unroll
-                for (int j = 0; j < 4; ++j) g[j] = gelu_fast(x[j]);
+                for (int h = 0; h < 2; ++h) {
+                    const float xp = sc * (float)(2 * lane + h + 1);
+                    const float q = gelu_tail_q(xp);
+                    x[2 * h] = xp;
+                    g[2 * h] = xp - xp * q;
+                    x[2 * h + 1] = -xp;
+                    g[2 * h + 1] = -xp * q;
+                }
                 s2 = block_scale(gtop);
                 table_codes(g, x, s2, code);
+                uint8_t *tb = reinterpret_cast<uint8_t *>(tables[wave][bb]);
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int pc = 2 * lane + h + 1;
+                    if (pc < 128) tb[pc] = (uint8_t)code[2 * h];
+                    tb[256 - pc] = (uint8_t)code[2 * h + 1];
+                }
+                if (lane == 0) tb[0] = 0;
             } else {
+                // entries u = 4*lane + j, code (int8_t)u
+#pragma unroll
+                for (int j = 0; j < 4; ++j) x[j] = sc * (float)(int8_t)(4 * lane + j);
                 // Rare: the block's largest |g| may sit on a negative code.
                 // The whole table is evaluated with the reference formula
                 // and the block's elements look up their |g| in it.
@@ -205,8 +225,8 @@ __global__ __launch_bounds__(256) void k_gelu_i8(const int8_t *__restrict__ q, i
                 // only the lanes of block bb count
                 s2 = block_scale(__uint_as_float(block_max_u(group_reduce_rows(__float_as_uint(m)), bb)));
                 if (s2 != 0.0f) quant_codes(g, s2, code);
+                tables[wave][bb][lane] = pack4(code[0], code[1], code[2], code[3]);
             }
-            tables[wave][bb][lane] = pack4(code[0], code[1], code[2], code[3]);
             if (lane == 0) so[gi * nbc + gj0 + bb] = s2;
         }
 

@@ -29,13 +29,15 @@ __device__ __forceinline__ float gelu_ref(float x) {
 // |x| >= 2^-10 (and x = 0) its error against gelu_ref is at most 6.51e-7
 // relative for x >= 0 and 2.14e-7 absolute for x < 0 (checked exhaustively;
 // the table path only evaluates such inputs).
-__device__ __forceinline__ float gelu_fast(float x) {
-    const float z = fabsf(x);
+__device__ __forceinline__ float gelu_tail_q(float z) {   // Q(z), z >= 0
     const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(0.2316419f, z, 1.0f));
     const float c1 = 0.127414796f, c2 = -0.142248368f, c3 = 0.710706871f, c4 = -0.726576013f,
                 c5 = 0.530702714f;
     const float poly = t * __builtin_fmaf(t, __builtin_fmaf(t, __builtin_fmaf(t, __builtin_fmaf(t, c5, c4), c3), c2), c1);
-    const float q = __builtin_amdgcn_exp2f(-0.72134752044448170368f * z * z) * poly;   // exp(-z^2/2) = 2^(-z^2/(2 ln 2))
+    return __builtin_amdgcn_exp2f(-0.72134752044448170368f * z * z) * poly;   // exp(-z^2/2) = 2^(-z^2/(2 ln 2))
+}
+__device__ __forceinline__ float gelu_fast(float x) {
+    const float q = gelu_tail_q(fabsf(x));
     return x >= 0.0f ? x - x * q : x * q;
 }
 
