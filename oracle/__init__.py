@@ -75,6 +75,9 @@ def _load():
         lib.jfo_gelu_bwd.argtypes = [ptr, ptr, ptr, ptr, i64, i64, ptr, ptr]
         lib.jfo_gelu_grad_value.argtypes = [ctypes.c_float]
         lib.jfo_gelu_grad_value.restype = ctypes.c_float
+        lib.jfo_quant_groups.argtypes = [ctypes.c_int, i64, i64]
+        lib.jfo_quant_groups.restype = i64
+        lib.jfo_quant_sse.argtypes = [ptr, i64, i64, ctypes.c_int, ptr, ptr]
         lib.jfo_set_threads.argtypes = [ctypes.c_int]
         lib.jfo_get_threads.restype = ctypes.c_int
         _lib = lib
@@ -235,3 +238,18 @@ def gelu_bwd(qdy: np.ndarray, sdy: np.ndarray, qx: np.ndarray, sx: np.ndarray):
     so = np.empty((R // 32, C // 32), np.float32)
     _chk(_load().jfo_gelu_bwd(_p(qdy), _p(sdy), _p(qx), _p(sx), R, C, _p(qo), _p(so)), "gelu_bwd")
     return qo, so
+
+
+GRANULARITIES = {"block": 0, "token": 1, "channel": 2, "tensor": 3}
+
+
+def quant_sse(x: np.ndarray, granularity: str):
+    """Scales and sum of squared quantization errors for one scale granularity
+    ('block' 32x32, 'token' per row, 'channel' per column, 'tensor')."""
+    x = _c(x, np.float32)
+    R, C = x.shape
+    g = GRANULARITIES[granularity]
+    s = np.empty(int(_load().jfo_quant_groups(g, R, C)), np.float32)
+    sse = np.zeros(1, np.float64)
+    _chk(_load().jfo_quant_sse(_p(x), R, C, g, _p(s), _p(sse)), "quant_sse")
+    return s, float(sse[0])

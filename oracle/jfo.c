@@ -37,6 +37,7 @@
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 #include <omp.h>
 
@@ -351,6 +352,78 @@ int jfo_gelu_bwd(const int8_t *qdy, const float *sdy, const int8_t *qx, const fl
             }
         quantize_one_block(tile, JFO_B, qo + bi * JFO_B * cols + bj * JFO_B, cols, &so[b]);
     }
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* Quantization error by scale granularity ("Measured effects": the   */
+/* per-block vs per-token and per-channel quantization-error          */
+/* ablations).  The same scale/code rule on four group shapes:        */
+/*   0: 32x32 blocks, 1: per token (one scale per row),               */
+/*   2: per channel (one per column), 3: per tensor (one scale).      */
+/* Returns the group scales (row-major over the group grid) and the   */
+/* sum of squared errors sum (x - fl(s*q))^2, accumulated in binary64 */
+/* (the difference of two binary32 values is exact in binary64).      */
+/* ------------------------------------------------------------------ */
+
+static int64_t group_of(int gran, int64_t rows, int64_t cols, int64_t r, int64_t c)
+{
+    switch (gran) {
+    case 0: return (r / JFO_B) * (cols / JFO_B) + c / JFO_B;
+    case 1: return r;
+    case 2: return c;
+    default: return 0;
+    }
+}
+
+int64_t jfo_quant_groups(int gran, int64_t rows, int64_t cols)
+{
+    switch (gran) {
+    case 0: return (rows / JFO_B) * (cols / JFO_B);
+    case 1: return rows;
+    case 2: return cols;
+    case 3: return 1;
+    default: return -1;
+    }
+}
+
+int jfo_quant_sse(const float *x, int64_t rows, int64_t cols, int gran, float *s, double *sse)
+{
+    if (!shape_ok(rows, cols) || gran < 0 || gran > 3) return -1;
+    const int64_t ng = jfo_quant_groups(gran, rows, cols);
+    for (int64_t g = 0; g < ng; ++g) s[g] = 0.0f;
+    /* group maxima (exact), then s = fl(max / 127) */
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < cols; ++c) {
+            int64_t g = group_of(gran, rows, cols, r, c);
+            float a = fabsf(x[r * cols + c]);
+            if (a > s[g]) s[g] = a;
+        }
+    for (int64_t g = 0; g < ng; ++g) s[g] = s[g] / 127.0f;
+    /* per-row sums in parallel, then summed in row order: deterministic */
+    double *rowsum = (double *)malloc((size_t)rows * sizeof(double));
+    if (!rowsum) return -2;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        double row = 0.0;
+        for (int64_t c = 0; c < cols; ++c) {
+            float sg = s[group_of(gran, rows, cols, r, c)];
+            float xv = x[r * cols + c], xh = 0.0f;
+            if (sg != 0.0f) {
+                float v = rintf(xv / sg);
+                if (v > 127.0f) v = 127.0f;
+                if (v < -127.0f) v = -127.0f;
+                xh = sg * v;
+            }
+            double d = (double)xv - (double)xh;
+            row += d * d;
+        }
+        rowsum[r] = row;
+    }
+    double total = 0.0;
+    for (int64_t r = 0; r < rows; ++r) total += rowsum[r];
+    free(rowsum);
+    *sse = total;
     return 0;
 }
 
