@@ -277,6 +277,35 @@ def bf16_reference(step, steps):
     return ms
 
 
+def quant_error_section(step, reps=10):
+    """jf_quant_error on the step's input activations X (8192 x 4096, outlier
+    columns): per scale granularity the mean squared quantization error and
+    the kernels' time.  Block scales take one pass over X; rows, columns and
+    the tensor take two (maxima, then errors)."""
+    import torch
+
+    jf = step.jf
+    x = step.fp["X"]
+    n = x.numel()
+    res = {}
+    for gran in ("block", "token", "channel", "tensor"):
+        s, e = jf.quant_error(x, gran)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            jf.quant_error(x, gran, s, e)
+        b.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) / reps * 1e3
+        passes = 1 if gran == "block" else 2
+        res[gran] = {"mse": float(e.item()) / n, "us": round(us, 1),
+                     "read_gbs": round(passes * 4 * n / (us * 1e-6) / 1e9, 1), "passes": passes}
+    res["block_vs_token_mse"] = round(res["block"]["mse"] / res["token"]["mse"], 4)
+    res["what"] = "X 8192x4096 (N(0,1), 0.5% of columns x100): sum (x - s q)^2 / n per scale granularity"
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -375,6 +404,8 @@ def main():
                 "what": "the 12 GEMM shapes as torch.mm in bfloat16 (vendor BLAS), operands pre-laid-out, "
                         "bf16 outputs; compared with the INT8 GEMMs' time in the step"}
 
+    qerr = quant_error_section(step)
+
     cpu = None
     if args.cpu_seconds > 0:
         try:
@@ -405,6 +436,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "bf16_reference": bf16,
+        "quant_error": qerr,
         "kernels": kernels,
         "host_wall_s": round(wall, 3),
     }

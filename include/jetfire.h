@@ -36,10 +36,12 @@
  *        JF_ERR_SHAPE  a size is negative or not a multiple of 32
  *        JF_ERR_LD     a leading dimension is below the row length, or its
  *                      row pitch is not a multiple of 16 bytes
- *        JF_ERR_ALIGN  a matrix base is not 16-byte aligned, or a scale grid
- *                      base is not 4-byte aligned
+ *        JF_ERR_ALIGN  a matrix base is not 16-byte aligned, a scale grid
+ *                      base is not 4-byte aligned, or a binary64 sum is not
+ *                      8-byte aligned
  *        JF_ERR_DTYPE  an unknown element type / output kind
- *        JF_ERR_ARG    a transpose flag other than 0 or 1
+ *        JF_ERR_ARG    a transpose flag other than 0 or 1, or an unknown
+ *                      scale granularity
  *        JF_ERR_ALIAS  an output overlaps an input or another output
  *        JF_ERR_HIP    the kernel launch failed (hipGetLastError)
  *    A size of zero is valid: nothing is launched for an empty output, and a
@@ -57,7 +59,7 @@
 extern "C" {
 #endif
 
-#define JF_ABI_VERSION 2
+#define JF_ABI_VERSION 3
 
 #ifndef JF_API
 #define JF_API __attribute__((visibility("default")))
@@ -80,6 +82,10 @@ typedef enum jf_dtype { JF_F32 = 0, JF_BF16 = 1 } jf_dtype;
 
 /* Output kind of the GEMM. */
 typedef enum jf_out { JF_OUT_I8 = 0, JF_OUT_F32 = 1 } jf_out;
+
+/* Scale granularity of jf_quant_error: one scale per 32x32 block, per row
+ * (token), per column (channel) or for the whole matrix (tensor). */
+typedef enum jf_gran { JF_GRAN_BLOCK = 0, JF_GRAN_TOKEN = 1, JF_GRAN_CHANNEL = 2, JF_GRAN_TENSOR = 3 } jf_gran;
 
 /*
  * jf_quantize_block -- per-block INT8 quantization of a high-precision matrix.
@@ -163,6 +169,29 @@ JF_API jf_status jf_gelu_i8(const int8_t *q, int64_t ldq, const float *s, int64_
 JF_API jf_status jf_gelu_bwd_i8(const int8_t *qdy, int64_t lddy, const float *sdy, const int8_t *qx, int64_t ldx,
                                 const float *sx, int64_t rows, int64_t cols, int8_t *qo, int64_t ldo, float *so,
                                 hipStream_t stream);
+
+/*
+ * jf_quant_error -- quantization error of one binary32 matrix under one scale
+ * granularity.  Pages: "Jetfire" summary, "Measured effects" (per-block
+ * quantization keeps the error of activations with channel-wise outliers
+ * below per-token and per-channel quantization).
+ *
+ *   x, ldx       rows x cols binary32 matrix (16-byte aligned rows)
+ *   granularity  a jf_gran value
+ *   s            group scales, written: (rows/32) x (cols/32) row-major for
+ *                JF_GRAN_BLOCK, rows for TOKEN, cols for CHANNEL, 1 for
+ *                TENSOR (4-byte aligned)
+ *   sse          one binary64, written: sum over all elements of
+ *                (x - fl(s*q))^2, each term in binary64 (8-byte aligned)
+ * Each group takes the per-block rule: s = fl(max|x|/127),
+ * q = clamp(rne(fl(x/s)), -127, 127), fl(s*q) = 0 when s = 0.  Scales are
+ * exact; sse is summed in an unspecified order (binary64 rounding only).
+ * The codes are not stored.  sse is required; with rows or cols zero the
+ * scales that exist are set to zero and sse to 0.  s and sse may not overlap
+ * x or each other.
+ */
+JF_API jf_status jf_quant_error(const float *x, int64_t ldx, int64_t rows, int64_t cols, int granularity,
+                                float *s, double *sse, hipStream_t stream);
 
 /* Human-readable name of a status code (static storage). */
 JF_API const char *jf_status_str(jf_status status);

@@ -54,9 +54,9 @@ const char *jf_status_str(jf_status st) {
         case JF_ERR_NULL: return "null pointer";
         case JF_ERR_SHAPE: return "size negative or not a multiple of 32";
         case JF_ERR_LD: return "leading dimension below row length or row pitch not a multiple of 16 bytes";
-        case JF_ERR_ALIGN: return "pointer misaligned (matrices 16 bytes, scales 4 bytes)";
+        case JF_ERR_ALIGN: return "pointer misaligned (matrices 16 bytes, scales 4 bytes, sums 8 bytes)";
         case JF_ERR_DTYPE: return "unknown element type or output kind";
-        case JF_ERR_ARG: return "transpose flag not 0 or 1";
+        case JF_ERR_ARG: return "transpose flag not 0 or 1, or unknown scale granularity";
         case JF_ERR_ALIAS: return "an output overlaps an input or another output";
         case JF_ERR_HIP: return "HIP kernel launch failed";
     }
@@ -150,6 +150,24 @@ jf_status jf_gelu_bwd_i8(const int8_t *qdy, int64_t lddy, const float *sdy, cons
     if (overlap(rqo, rso)) return JF_ERR_ALIAS;
     if (rows == 0 || cols == 0) return JF_OK;
     return hip_status(jf::launch_gelu_bwd(qdy, lddy, sdy, qx, ldx, sx, rows, cols, qo, ldo, so, stream));
+}
+
+jf_status jf_quant_error(const float *x, int64_t ldx, int64_t rows, int64_t cols, int granularity, float *s,
+                         double *sse, hipStream_t stream) {
+    // number of scales; an unknown granularity needs s too (rejected below)
+    const bool known = granularity >= JF_GRAN_BLOCK && granularity <= JF_GRAN_TENSOR;
+    const int64_t ng = granularity == JF_GRAN_BLOCK ? (rows / kB) * (cols / kB)
+                       : granularity == JF_GRAN_TOKEN ? rows
+                       : granularity == JF_GRAN_CHANNEL ? cols
+                                                        : 1;
+    if (missing(x, rows, cols) || !sse || (!s && (ng != 0 || !known))) return JF_ERR_NULL;
+    if (!shape_ok(rows) || !shape_ok(cols)) return JF_ERR_SHAPE;
+    if (!ld_ok(ldx, cols, 4)) return JF_ERR_LD;
+    if (!aligned(x, 16) || !aligned(s, 4) || !aligned(sse, 8)) return JF_ERR_ALIGN;
+    if (!known) return JF_ERR_ARG;
+    const Range rx = span(x, rows, cols, ldx, 4), rs = span(s, 1, ng, ng, 4), re = span(sse, 1, 1, 1, 8);
+    if (overlap(rx, rs) || overlap(rx, re) || overlap(rs, re)) return JF_ERR_ALIAS;
+    return hip_status(jf::launch_quant_error(x, ldx, rows, cols, granularity, s, sse, stream));
 }
 
 }  // extern "C"

@@ -23,4 +23,8 @@ hipError_t launch_gelu_bwd(const int8_t *qdy, int64_t lddy, const float *sdy, co
                            const float *sx, int64_t rows, int64_t cols, int8_t *qo, int64_t ldo, float *so,
                            hipStream_t stream);
 
+// granularity: 0 block, 1 token (row), 2 channel (column), 3 tensor
+hipError_t launch_quant_error(const float *x, int64_t ldx, int64_t rows, int64_t cols, int granularity, float *s,
+                              double *sse, hipStream_t stream);
+
 }  // namespace jf

@@ -7,7 +7,7 @@ stream).  There is no fallback: if the library is missing, importing this
 module raises.
 
 Names follow the C ABI:  quantize_block, gemm_i8_blockscaled, requant_block,
-gelu_i8.  A tensor argument is a 2-D CUDA(HIP) tensor whose last dimension is
+gelu_i8, gelu_bwd_i8, quant_error.  A tensor argument is a 2-D CUDA(HIP) tensor whose last dimension is
 contiguous; its row stride is passed as the leading dimension.
 """
 from __future__ import annotations
@@ -24,10 +24,11 @@ JF_OK, JF_ERR_NULL, JF_ERR_SHAPE, JF_ERR_LD, JF_ERR_ALIGN = 0, 1, 2, 3, 4
 JF_ERR_DTYPE, JF_ERR_ARG, JF_ERR_ALIAS, JF_ERR_HIP = 5, 6, 7, 8
 JF_F32, JF_BF16 = 0, 1
 JF_OUT_I8, JF_OUT_F32 = 0, 1
+GRANULARITIES = {"block": 0, "token": 1, "channel": 2, "tensor": 3}
 
 # Every symbol include/jetfire.h declares.
 EXPORTS = ("jf_quantize_block", "jf_gemm_i8_blockscaled", "jf_requant_block", "jf_gelu_i8",
-           "jf_gelu_bwd_i8", "jf_status_str", "jf_abi_version")
+           "jf_gelu_bwd_i8", "jf_quant_error", "jf_status_str", "jf_abi_version")
 
 
 class JetfireError(RuntimeError):
@@ -52,6 +53,8 @@ def _load() -> ctypes.CDLL:
     lib.jf_gelu_i8.restype = cint
     lib.jf_gelu_bwd_i8.argtypes = [ptr, i64, ptr, ptr, i64, ptr, i64, i64, ptr, i64, ptr, ptr]
     lib.jf_gelu_bwd_i8.restype = cint
+    lib.jf_quant_error.argtypes = [ptr, i64, i64, i64, cint, ptr, ptr, ptr]
+    lib.jf_quant_error.restype = cint
     lib.jf_status_str.argtypes = [cint]
     lib.jf_status_str.restype = ctypes.c_char_p
     lib.jf_abi_version.restype = cint
@@ -87,7 +90,8 @@ def _mat(t: torch.Tensor, name: str) -> int:
         raise ValueError(f"{name} must be a device tensor (the HIP path has no CPU fallback)")
     if t.shape[1] > 1 and t.stride(1) != 1:
         raise ValueError(f"{name} must have a contiguous last dimension")
-    return int(t.stride(0)) if t.shape[0] > 1 else int(t.shape[1])
+    # an empty or one-row matrix has no meaningful row stride: pass the row length
+    return int(t.stride(0)) if t.shape[0] > 1 and t.numel() > 0 else int(t.shape[1])
 
 
 def _scales(t: torch.Tensor, rows: int, cols: int, name: str) -> None:
@@ -202,3 +206,31 @@ def gelu_bwd_i8(qdy: torch.Tensor, sdy: torch.Tensor, qx: torch.Tensor, sx: torc
     _check(lib.jf_gelu_bwd_i8(_ptr(qdy), lddy, _ptr(sdy), _ptr(qx), ldx, _ptr(sx), R, C, _ptr(qo), ldo, _ptr(so),
                               _stream(qx.device)), "jf_gelu_bwd_i8")
     return qo, so
+
+
+def scale_count(granularity: str, rows: int, cols: int) -> int:
+    g = GRANULARITIES[granularity]
+    return (rows // 32) * (cols // 32) if g == 0 else rows if g == 1 else cols if g == 2 else 1
+
+
+def quant_error(x: torch.Tensor, granularity: str, s: torch.Tensor | None = None,
+                sse: torch.Tensor | None = None):
+    """jf_quant_error: group scales (1-D float32) and the binary64 sum of squared
+    quantization errors (1-element float64 tensor) of a float32 matrix under
+    'block' (32x32), 'token', 'channel' or 'tensor' scaling."""
+    ldx = _mat(x, "x")
+    if x.dtype != torch.float32:
+        raise ValueError("x must be float32")
+    if granularity not in GRANULARITIES:
+        raise ValueError(f"granularity must be one of {sorted(GRANULARITIES)}")
+    R, C = x.shape
+    n = scale_count(granularity, R, C)
+    s = torch.empty(n, dtype=torch.float32, device=x.device) if s is None else s
+    sse = torch.empty(1, dtype=torch.float64, device=x.device) if sse is None else sse
+    if s.dtype != torch.float32 or not s.is_cuda or s.numel() != n or not s.is_contiguous():
+        raise ValueError(f"s must be a contiguous float32 device tensor of {n} elements")
+    if sse.dtype != torch.float64 or not sse.is_cuda or sse.numel() != 1:
+        raise ValueError("sse must be a one-element float64 device tensor")
+    _check(lib.jf_quant_error(_ptr(x), ldx, R, C, GRANULARITIES[granularity], _ptr(s), _ptr(sse),
+                              _stream(x.device)), "jf_quant_error")
+    return s, sse

@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert jf.abi_version() == 2
+    assert jf.abi_version() == 3
     for st in range(0, 9):
         assert jf.status_str(st) and jf.status_str(st) != "unknown status"
     assert jf.status_str(99) == "unknown status"
@@ -113,6 +113,26 @@ def test_gelu_bwd_validation_codes():
     assert g(dy, 64, sdy, x, 64, sx, 64, 64, P(BASE + 0x20000100), 64, so, None) == jf.JF_ERR_ALIAS
     assert g(dy, 64, sdy, x, 64, sx, 64, 64, qo, 64, sx, None) == jf.JF_ERR_ALIAS
     assert g(dy, 64, sdy, x, 64, sx, 0, 64, qo, 64, so, None) == jf.JF_OK             # empty
+
+
+def test_quant_error_validation_codes():
+    q = jf.lib.jf_quant_error
+    x, s, e = P(BASE), P(BASE + 0x10000000), P(BASE + 0x20000000)
+    assert q(None, 64, 64, 64, 0, s, e, None) == jf.JF_ERR_NULL
+    assert q(x, 64, 64, 64, 0, s, None, None) == jf.JF_ERR_NULL          # the sum is always required
+    assert q(x, 64, 64, 64, 3, None, e, None) == jf.JF_ERR_NULL          # one tensor scale even if empty
+    assert q(x, 64, 64, 64, 9, None, e, None) == jf.JF_ERR_NULL          # unknown granularity: s required
+    assert q(x, 64, 64, 48, 0, s, e, None) == jf.JF_ERR_SHAPE
+    assert q(x, 64, -32, 64, 1, s, e, None) == jf.JF_ERR_SHAPE
+    assert q(x, 32, 64, 64, 0, s, e, None) == jf.JF_ERR_LD               # below the row length
+    assert q(x, 66, 64, 64, 0, s, e, None) == jf.JF_ERR_LD               # 264-byte pitch
+    assert q(P(BASE + 4), 64, 64, 64, 0, s, e, None) == jf.JF_ERR_ALIGN
+    assert q(x, 64, 64, 64, 0, P(BASE + 0x10000002), e, None) == jf.JF_ERR_ALIGN
+    assert q(x, 64, 64, 64, 0, s, P(BASE + 0x20000004), None) == jf.JF_ERR_ALIGN
+    assert q(x, 64, 64, 64, 4, s, e, None) == jf.JF_ERR_ARG
+    assert q(x, 64, 64, 64, -1, s, e, None) == jf.JF_ERR_ARG
+    assert q(x, 64, 64, 64, 1, P(BASE + 64 * 64 * 4 - 4), e, None) == jf.JF_ERR_ALIAS   # s over x's last row
+    assert q(x, 64, 64, 64, 2, s, P(BASE + 0x10000000 + 4 * 62), None) == jf.JF_ERR_ALIAS  # sse over s
 
 
 def test_binding_refuses_host_tensors():
