@@ -78,6 +78,8 @@ def _load():
         lib.jfo_quant_groups.argtypes = [ctypes.c_int, i64, i64]
         lib.jfo_quant_groups.restype = i64
         lib.jfo_quant_sse.argtypes = [ptr, i64, i64, ctypes.c_int, ptr, ptr]
+        lib.jfo_add.argtypes = [ptr, ptr, ptr, ptr, i64, i64, ptr, ptr]
+        lib.jfo_layernorm.argtypes = [ptr, ptr, i64, i64, ptr, ptr, ctypes.c_float, ptr, ptr, ptr, ptr]
         lib.jfo_set_threads.argtypes = [ctypes.c_int]
         lib.jfo_get_threads.restype = ctypes.c_int
         _lib = lib
@@ -238,6 +240,39 @@ def gelu_bwd(qdy: np.ndarray, sdy: np.ndarray, qx: np.ndarray, sx: np.ndarray):
     so = np.empty((R // 32, C // 32), np.float32)
     _chk(_load().jfo_gelu_bwd(_p(qdy), _p(sdy), _p(qx), _p(sx), R, C, _p(qo), _p(so)), "gelu_bwd")
     return qo, so
+
+
+def add(qa: np.ndarray, sa: np.ndarray, qb: np.ndarray, sb: np.ndarray):
+    """Residual add of two per-block INT8 tensors with the same blocking,
+    requantized per block: (codes, scales)."""
+    qa, qb = _c(qa, np.int8), _c(qb, np.int8)
+    sa, sb = _c(sa, np.float32), _c(sb, np.float32)
+    if qa.shape != qb.shape or sa.shape != sb.shape:
+        raise ValueError("operands must have the same shape and blocking")
+    R, C = qa.shape
+    qo = np.empty((R, C), np.int8)
+    so = np.empty((R // 32, C // 32), np.float32)
+    _chk(_load().jfo_add(_p(qa), _p(sa), _p(qb), _p(sb), R, C, _p(qo), _p(so)), "add")
+    return qo, so
+
+
+def layernorm(q: np.ndarray, s: np.ndarray, gamma: np.ndarray, beta: np.ndarray, eps: float = 1e-5,
+              stats: bool = False):
+    """LayerNorm over each row of a per-block INT8 tensor, requantized per
+    block: (codes, scales), plus (mean, rstd) per row in binary64 if stats."""
+    q = _c(q, np.int8)
+    s = _c(s, np.float32)
+    gamma, beta = _c(gamma, np.float32), _c(beta, np.float32)
+    R, C = q.shape
+    if gamma.shape != (C,) or beta.shape != (C,):
+        raise ValueError("gamma and beta must have one value per column")
+    qo = np.empty((R, C), np.int8)
+    so = np.empty((R // 32, C // 32), np.float32)
+    mean = np.empty(R, np.float64)
+    rstd = np.empty(R, np.float64)
+    _chk(_load().jfo_layernorm(_p(q), _p(s), R, C, _p(gamma), _p(beta), float(np.float32(eps)), _p(qo), _p(so),
+                               _p(mean), _p(rstd)), "layernorm")
+    return (qo, so, mean, rstd) if stats else (qo, so)
 
 
 GRANULARITIES = {"block": 0, "token": 1, "channel": 2, "tensor": 3}

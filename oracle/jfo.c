@@ -29,7 +29,14 @@
  *     is requantized with the same scale/code rule;
  *   - GELU backward: dy = fl(s_dy * q_dy), x = fl(s_x * q_x),
  *     g' = Phi(x) + x phi(x) in binary64 rounded once, y = fl(dy * g'),
- *     then the same per-block requantization.
+ *     then the same per-block requantization;
+ *   - residual add of two tensors with the same blocking:
+ *     z = fl(fl(s_a * q_a) + fl(s_b * q_b)), then the per-block rule;
+ *   - LayerNorm over each row (the hidden dimension): x = fl(s * q);
+ *     mean m = (sum x) / n and variance v = (sum (x - m)^2) / n in binary64,
+ *     summed in column order; r = 1 / sqrt(v + eps) in binary64;
+ *     y = ((x - m) * r) * gamma + beta in binary64, rounded once to binary32;
+ *     then the per-block rule on y.
  *
  * Build: gcc -O2 -fopenmp -ffp-contract=off (no contraction, no fast-math),
  * so every rounding below is the one written.  All matrices are dense,
@@ -353,6 +360,70 @@ int jfo_gelu_bwd(const int8_t *qdy, const float *sdy, const int8_t *qx, const fl
         quantize_one_block(tile, JFO_B, qo + bi * JFO_B * cols + bj * JFO_B, cols, &so[b]);
     }
     return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* Residual add and LayerNorm with INT8 in and out ("Approach": every   */
+/* operator of the data flow reads and writes per-block INT8).          */
+/* ------------------------------------------------------------------ */
+
+int jfo_add(const int8_t *qa, const float *sa, const int8_t *qb, const float *sb,
+            int64_t rows, int64_t cols, int8_t *qo, float *so)
+{
+    if (!shape_ok(rows, cols)) return -1;
+    const int64_t bc = cols / JFO_B;
+#pragma omp parallel for schedule(static)
+    for (int64_t b = 0; b < (rows / JFO_B) * bc; ++b) {
+        int64_t bi = b / bc, bj = b % bc;
+        float tile[JFO_B * JFO_B];
+        for (int r = 0; r < JFO_B; ++r)
+            for (int c = 0; c < JFO_B; ++c) {
+                int64_t at = (bi * JFO_B + r) * cols + bj * JFO_B + c;
+                float a = sa[b] * (float)qa[at];
+                float bv = sb[b] * (float)qb[at];
+                tile[r * JFO_B + c] = a + bv;
+            }
+        quantize_one_block(tile, JFO_B, qo + bi * JFO_B * cols + bj * JFO_B, cols, &so[b]);
+    }
+    return 0;
+}
+
+/* mean and rstd (optional, may be NULL) receive m and r of every row. */
+int jfo_layernorm(const int8_t *q, const float *s, int64_t rows, int64_t cols, const float *gamma,
+                  const float *beta, float eps, int8_t *qo, float *so, double *mean, double *rstd)
+{
+    if (!shape_ok(rows, cols)) return -1;
+    const int64_t bc = cols / JFO_B;
+    int bad = 0;
+#pragma omp parallel for schedule(static)
+    for (int64_t bi = 0; bi < rows / JFO_B; ++bi) {
+        float *y = (float *)malloc((size_t)(JFO_B * cols) * sizeof(float));
+        if (!y) { bad = 1; continue; }
+        for (int r = 0; r < JFO_B; ++r) {
+            const int64_t row = bi * JFO_B + r;
+            double sum = 0.0;
+            for (int64_t c = 0; c < cols; ++c)
+                sum += (double)(s[bi * bc + c / JFO_B] * (float)q[row * cols + c]);
+            const double m = sum / (double)cols;
+            double sq = 0.0;
+            for (int64_t c = 0; c < cols; ++c) {
+                double d = (double)(s[bi * bc + c / JFO_B] * (float)q[row * cols + c]) - m;
+                sq += d * d;
+            }
+            const double v = sq / (double)cols;
+            const double rs = 1.0 / sqrt(v + (double)eps);
+            if (mean) mean[row] = m;
+            if (rstd) rstd[row] = rs;
+            for (int64_t c = 0; c < cols; ++c) {
+                double x = (double)(s[bi * bc + c / JFO_B] * (float)q[row * cols + c]);
+                y[r * cols + c] = (float)(((x - m) * rs) * (double)gamma[c] + (double)beta[c]);
+            }
+        }
+        for (int64_t bj = 0; bj < bc; ++bj)
+            quantize_one_block(y + bj * JFO_B, cols, qo + bi * JFO_B * cols + bj * JFO_B, cols, &so[bi * bc + bj]);
+        free(y);
+    }
+    return bad ? -2 : 0;
 }
 
 /* ------------------------------------------------------------------ */
