@@ -40,8 +40,8 @@
  *                      base is not 4-byte aligned, or a binary64 sum is not
  *                      8-byte aligned
  *        JF_ERR_DTYPE  an unknown element type / output kind
- *        JF_ERR_ARG    a transpose flag other than 0 or 1, or an unknown
- *                      scale granularity
+ *        JF_ERR_ARG    a transpose flag other than 0 or 1, an unknown scale
+ *                      granularity, or a negative or non-finite epsilon
  *        JF_ERR_ALIAS  an output overlaps an input or another output
  *        JF_ERR_HIP    the kernel launch failed (hipGetLastError)
  *    A size of zero is valid: nothing is launched for an empty output, and a
@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define JF_ABI_VERSION 3
+#define JF_ABI_VERSION 4
 
 #ifndef JF_API
 #define JF_API __attribute__((visibility("default")))
@@ -169,6 +169,44 @@ JF_API jf_status jf_gelu_i8(const int8_t *q, int64_t ldq, const float *s, int64_
 JF_API jf_status jf_gelu_bwd_i8(const int8_t *qdy, int64_t lddy, const float *sdy, const int8_t *qx, int64_t ldx,
                                 const float *sx, int64_t rows, int64_t cols, int8_t *qo, int64_t ldo, float *so,
                                 hipStream_t stream);
+
+/*
+ * jf_add_i8 -- residual add of two per-block INT8 tensors.  Pages: "Jetfire"
+ * summary, "Approach" (every operator of the data flow reads and writes INT8
+ * with one scale per 32x32 block; the add itself is this library's reading).
+ *
+ *   qa, sa    rows x cols codes (lda) and scale grid of the first operand
+ *   qb, sb    the second operand, same 32x32 blocking (ldb)
+ *   qo, so    rows x cols output codes (ldo) and scale grid
+ * Per element z = fl(fl(sa*qa) + fl(sb*qb)); then the per-block rule on z.
+ * Outputs may not overlap inputs.
+ */
+JF_API jf_status jf_add_i8(const int8_t *qa, int64_t lda, const float *sa, const int8_t *qb, int64_t ldb,
+                           const float *sb, int64_t rows, int64_t cols, int8_t *qo, int64_t ldo, float *so,
+                           hipStream_t stream);
+
+/*
+ * jf_layernorm_i8 -- LayerNorm over each row (the hidden dimension) of a
+ * per-block INT8 tensor, INT8 out.  Pages: "Jetfire" summary, "Approach"
+ * (every operator of the data flow reads and writes per-block INT8; the
+ * normalization itself is this library's reading).
+ *
+ *   q, s         rows x cols input codes (ldq) and scale grid
+ *   gamma, beta  cols binary32 values each (16-byte aligned)
+ *   eps          added to the variance; finite and >= 0 (rows of zero
+ *                variance need eps > 0)
+ *   qo, so       rows x cols output codes (ldo) and scale grid
+ *   mean, rstd   optional (NULL to skip): rows binary64 values each, the
+ *                row means and 1/sqrt(v + eps) (8-byte aligned)
+ * Per row: x = fl(s*q); m = sum(x)/n and v = sum((x - m)^2)/n in binary64;
+ * r = 1/sqrt(v + eps) in binary64; y = ((x - m)*r)*gamma + beta in binary64
+ * rounded once to binary32; then the per-block rule on y.  The binary64 sums
+ * are formed in an unspecified order.  Outputs may not overlap inputs or
+ * each other.
+ */
+JF_API jf_status jf_layernorm_i8(const int8_t *q, int64_t ldq, const float *s, int64_t rows, int64_t cols,
+                                 const float *gamma, const float *beta, float eps, int8_t *qo, int64_t ldo,
+                                 float *so, double *mean, double *rstd, hipStream_t stream);
 
 /*
  * jf_quant_error -- quantization error of one binary32 matrix under one scale

@@ -56,7 +56,7 @@ const char *jf_status_str(jf_status st) {
         case JF_ERR_LD: return "leading dimension below row length or row pitch not a multiple of 16 bytes";
         case JF_ERR_ALIGN: return "pointer misaligned (matrices 16 bytes, scales 4 bytes, sums 8 bytes)";
         case JF_ERR_DTYPE: return "unknown element type or output kind";
-        case JF_ERR_ARG: return "transpose flag not 0 or 1, or unknown scale granularity";
+        case JF_ERR_ARG: return "transpose flag not 0 or 1, unknown scale granularity, or bad epsilon";
         case JF_ERR_ALIAS: return "an output overlaps an input or another output";
         case JF_ERR_HIP: return "HIP kernel launch failed";
     }
@@ -150,6 +150,53 @@ jf_status jf_gelu_bwd_i8(const int8_t *qdy, int64_t lddy, const float *sdy, cons
     if (overlap(rqo, rso)) return JF_ERR_ALIAS;
     if (rows == 0 || cols == 0) return JF_OK;
     return hip_status(jf::launch_gelu_bwd(qdy, lddy, sdy, qx, ldx, sx, rows, cols, qo, ldo, so, stream));
+}
+
+jf_status jf_add_i8(const int8_t *qa, int64_t lda, const float *sa, const int8_t *qb, int64_t ldb, const float *sb,
+                    int64_t rows, int64_t cols, int8_t *qo, int64_t ldo, float *so, hipStream_t stream) {
+    if (missing(qa, rows, cols) || missing(sa, rows, cols) || missing(qb, rows, cols) || missing(sb, rows, cols) ||
+        missing(qo, rows, cols) || missing(so, rows, cols))
+        return JF_ERR_NULL;
+    if (!shape_ok(rows) || !shape_ok(cols)) return JF_ERR_SHAPE;
+    if (!ld_ok(lda, cols, 1) || !ld_ok(ldb, cols, 1) || !ld_ok(ldo, cols, 1)) return JF_ERR_LD;
+    if (!aligned(qa, 16) || !aligned(qb, 16) || !aligned(qo, 16) || !aligned(sa, 4) || !aligned(sb, 4) ||
+        !aligned(so, 4))
+        return JF_ERR_ALIGN;
+    const int64_t gr = rows / kB, gc = cols / kB;
+    const Range rqo = span(qo, rows, cols, ldo, 1), rso = span(so, gr, gc, gc, 4);
+    for (Range in : {span(qa, rows, cols, lda, 1), span(sa, gr, gc, gc, 4), span(qb, rows, cols, ldb, 1),
+                     span(sb, gr, gc, gc, 4)})
+        if (overlap(rqo, in) || overlap(rso, in)) return JF_ERR_ALIAS;
+    if (overlap(rqo, rso)) return JF_ERR_ALIAS;
+    if (rows == 0 || cols == 0) return JF_OK;
+    return hip_status(jf::launch_add(qa, lda, sa, qb, ldb, sb, rows, cols, qo, ldo, so, stream));
+}
+
+jf_status jf_layernorm_i8(const int8_t *q, int64_t ldq, const float *s, int64_t rows, int64_t cols,
+                          const float *gamma, const float *beta, float eps, int8_t *qo, int64_t ldo, float *so,
+                          double *mean, double *rstd, hipStream_t stream) {
+    if (missing(q, rows, cols) || missing(s, rows, cols) || missing(gamma, rows, cols) ||
+        missing(beta, rows, cols) || missing(qo, rows, cols) || missing(so, rows, cols))
+        return JF_ERR_NULL;
+    if (!shape_ok(rows) || !shape_ok(cols)) return JF_ERR_SHAPE;
+    if (!ld_ok(ldq, cols, 1) || !ld_ok(ldo, cols, 1)) return JF_ERR_LD;
+    if (!aligned(q, 16) || !aligned(qo, 16) || !aligned(gamma, 16) || !aligned(beta, 16) || !aligned(s, 4) ||
+        !aligned(so, 4) || !aligned(mean, 8) || !aligned(rstd, 8))
+        return JF_ERR_ALIGN;
+    if (!(eps >= 0.0f) || !(eps < __builtin_inff())) return JF_ERR_ARG;
+    const int64_t gr = rows / kB, gc = cols / kB;
+    const Range rqo = span(qo, rows, cols, ldo, 1), rso = span(so, gr, gc, gc, 4);
+    const Range rm = mean ? span(mean, 1, rows, rows, 8) : Range{0, 0};
+    const Range rr = rstd ? span(rstd, 1, rows, rows, 8) : Range{0, 0};
+    for (Range in : {span(q, rows, cols, ldq, 1), span(s, gr, gc, gc, 4), span(gamma, 1, cols, cols, 4),
+                     span(beta, 1, cols, cols, 4)})
+        if (overlap(rqo, in) || overlap(rso, in) || overlap(rm, in) || overlap(rr, in)) return JF_ERR_ALIAS;
+    if (overlap(rqo, rso) || overlap(rqo, rm) || overlap(rqo, rr) || overlap(rso, rm) || overlap(rso, rr) ||
+        overlap(rm, rr))
+        return JF_ERR_ALIAS;
+    if (rows == 0 || cols == 0) return JF_OK;
+    return hip_status(jf::launch_layernorm(q, ldq, s, rows, cols, gamma, beta, eps, qo, ldo, so, mean, rstd,
+                                           stream));
 }
 
 jf_status jf_quant_error(const float *x, int64_t ldx, int64_t rows, int64_t cols, int granularity, float *s,

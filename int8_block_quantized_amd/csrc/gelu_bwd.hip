@@ -18,7 +18,7 @@
 // |y| (DPP within rows of 16 lanes, readlanes across them), s = fl(max/127)
 // and the exact codes of quant_codes.
 // HBM traffic: 2 bytes in + 1 byte out per element, 12 bytes per block.
-#include "jf_device.h"
+#include "jf_group.h"
 #include "jf_launch.h"
 
 namespace jf {
@@ -27,7 +27,7 @@ namespace {
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) const float lds_f32;
 
-constexpr int kGroup = 4;   // horizontally adjacent blocks per wavefront
+constexpr int kGroup = kGroupBlocks;   // horizontally adjacent blocks per wavefront
 
 // GELU' at x and -x (x >= 0) in binary64, each rounded once.  One erfc and
 // one exp serve both: Phi(x) = 1 - Q(x), Phi(-x) = Q(x) with
@@ -38,17 +38,6 @@ __device__ __attribute__((noinline)) float2 gelu_grad_pair(float x) {
     const double q = 0.5 * erfc(xd * 0.70710678118654752440);
     const double xpdf = xd * (exp(-0.5 * xd * xd) * 0.39894228040143267794);
     return make_float2((float)((1.0 - q) + xpdf), (float)(q - xpdf));
-}
-
-// Maximum over the 16 lanes holding one block (lanes 8r + 2b + e): DPP over
-// lane bits 0 and 3 within rows of 16, then one readlane per row.
-__device__ __forceinline__ float block_max(float v, int b) {
-    uint32_t u = __float_as_uint(v);   // v >= 0: the IEEE order is the unsigned order
-    u = max(u, dpp<kDppXor1>(u));
-    u = max(u, dpp<kDppRowRor8>(u));
-    const uint32_t a = __builtin_amdgcn_readlane(u, 2 * b), c = __builtin_amdgcn_readlane(u, 16 + 2 * b);
-    const uint32_t d = __builtin_amdgcn_readlane(u, 32 + 2 * b), e = __builtin_amdgcn_readlane(u, 48 + 2 * b);
-    return __uint_as_float(max(max(a, c), max(d, e)));
 }
 
 __global__ __launch_bounds__(256) void k_gelu_bwd_i8(const int8_t *__restrict__ qdy, int64_t lddy,
@@ -122,29 +111,10 @@ __global__ __launch_bounds__(256) void k_gelu_bwd_i8(const int8_t *__restrict__ 
     }
     float sb[kGroup];
 #pragma unroll
-    for (int bb = 0; bb < kGroup; ++bb) sb[bb] = block_scale(block_max(m, bb));
-    const float sc = b == 0 ? sb[0] : b == 1 ? sb[1] : b == 2 ? sb[2] : sb[3];
-
-    if (gj0 + b < nbc) {
-        int8_t *dst = qo + (gi * kBlock + r8) * ldo + (int64_t)(gj0 + b) * kBlock + colb;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float v[16];
-#pragma unroll
-            for (int e = 0; e < 16; ++e) v[e] = y[16 * i + e];
-            int code[16];
-            if (sc != 0.0f) {
-                quant_codes(v, sc, code);
-            } else {
-#pragma unroll
-                for (int e = 0; e < 16; ++e) code[e] = 0;
-            }
-            *reinterpret_cast<u32x4 *>(dst + 8 * i * ldo) =
-                u32x4{pack4(code[0], code[1], code[2], code[3]), pack4(code[4], code[5], code[6], code[7]),
-                      pack4(code[8], code[9], code[10], code[11]), pack4(code[12], code[13], code[14], code[15])};
-        }
-    }
-    if (lane < nb) so[gi * nbc + gj0 + lane] = lane == 0 ? sb[0] : lane == 1 ? sb[1] : lane == 2 ? sb[2] : sb[3];
+    for (int bb = 0; bb < kGroup; ++bb) sb[bb] = block_scale(group_block_max(m, bb));
+    if (gj0 + b < nbc)
+        store_group_codes(y, pick4(sb, b), qo + (gi * kBlock + r8) * ldo + (int64_t)(gj0 + b) * kBlock + colb, ldo);
+    if (lane < nb) so[gi * nbc + gj0 + lane] = pick4(sb, lane);
 }
 
 }  // namespace

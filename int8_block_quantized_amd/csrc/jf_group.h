@@ -1,0 +1,53 @@
+// jf_group.h -- the "group of four blocks" mapping shared by the INT8 -> INT8
+// elementwise and row kernels (GELU backward, residual add, LayerNorm).
+//
+// A wavefront covers four horizontally adjacent 32x32 blocks (a 32 x 128
+// byte tile).  Lane l holds rows 8i + l/8 (i = 0..3) and bytes 16(l%8) ..
+// 16(l%8)+15 of each row, i.e. part of block (l%8)/2; every 16-byte load and
+// store of the wavefront spans eight whole 128-byte rows.
+#pragma once
+
+#include "jf_device.h"
+
+namespace jf {
+
+constexpr int kGroupBlocks = 4;
+
+// Maximum over the 16 lanes holding block b (lanes 8r + 2b + e): DPP over
+// lane bits 0 and 3 within rows of 16, then one readlane per row.  v >= 0,
+// whose IEEE order is the unsigned order of the bits.  Wave-uniform result.
+__device__ __forceinline__ float group_block_max(float v, int b) {
+    uint32_t u = __float_as_uint(v);
+    u = max(u, dpp<kDppXor1>(u));
+    u = max(u, dpp<kDppRowRor8>(u));
+    const uint32_t a = __builtin_amdgcn_readlane(u, 2 * b), c = __builtin_amdgcn_readlane(u, 16 + 2 * b);
+    const uint32_t d = __builtin_amdgcn_readlane(u, 32 + 2 * b), e = __builtin_amdgcn_readlane(u, 48 + 2 * b);
+    return __uint_as_float(max(max(a, c), max(d, e)));
+}
+
+// Codes of the lane's 4 x 16 values y (row-major by i) under scale sc,
+// stored as four 16-byte rows at dst + 8 i ld.  A zero scale stores zeros.
+__device__ __forceinline__ void store_group_codes(const float (&y)[64], float sc, int8_t *dst, int64_t ld) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float v[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) v[e] = y[16 * i + e];
+        int code[16];
+        if (sc != 0.0f) {
+            quant_codes(v, sc, code);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) code[e] = 0;
+        }
+        *reinterpret_cast<u32x4 *>(dst + 8 * i * ld) =
+            u32x4{pack4(code[0], code[1], code[2], code[3]), pack4(code[4], code[5], code[6], code[7]),
+                  pack4(code[8], code[9], code[10], code[11]), pack4(code[12], code[13], code[14], code[15])};
+    }
+}
+
+__device__ __forceinline__ float pick4(const float (&v)[4], int b) {
+    return b == 0 ? v[0] : b == 1 ? v[1] : b == 2 ? v[2] : v[3];
+}
+
+}  // namespace jf

@@ -23,6 +23,13 @@ hipError_t launch_gelu_bwd(const int8_t *qdy, int64_t lddy, const float *sdy, co
                            const float *sx, int64_t rows, int64_t cols, int8_t *qo, int64_t ldo, float *so,
                            hipStream_t stream);
 
+hipError_t launch_add(const int8_t *qa, int64_t lda, const float *sa, const int8_t *qb, int64_t ldb,
+                      const float *sb, int64_t rows, int64_t cols, int8_t *qo, int64_t ldo, float *so,
+                      hipStream_t stream);
+hipError_t launch_layernorm(const int8_t *q, int64_t ldq, const float *s, int64_t rows, int64_t cols,
+                            const float *gamma, const float *beta, float eps, int8_t *qo, int64_t ldo, float *so,
+                            double *mean, double *rstd, hipStream_t stream);
+
 // granularity: 0 block, 1 token (row), 2 channel (column), 3 tensor
 hipError_t launch_quant_error(const float *x, int64_t ldx, int64_t rows, int64_t cols, int granularity, float *s,
                               double *sse, hipStream_t stream);

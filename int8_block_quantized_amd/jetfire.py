@@ -7,7 +7,7 @@ stream).  There is no fallback: if the library is missing, importing this
 module raises.
 
 Names follow the C ABI:  quantize_block, gemm_i8_blockscaled, requant_block,
-gelu_i8, gelu_bwd_i8, quant_error.  A tensor argument is a 2-D CUDA(HIP) tensor whose last dimension is
+gelu_i8, gelu_bwd_i8, add_i8, layernorm_i8, quant_error.  A tensor argument is a 2-D CUDA(HIP) tensor whose last dimension is
 contiguous; its row stride is passed as the leading dimension.
 """
 from __future__ import annotations
@@ -28,7 +28,8 @@ GRANULARITIES = {"block": 0, "token": 1, "channel": 2, "tensor": 3}
 
 # Every symbol include/jetfire.h declares.
 EXPORTS = ("jf_quantize_block", "jf_gemm_i8_blockscaled", "jf_requant_block", "jf_gelu_i8",
-           "jf_gelu_bwd_i8", "jf_quant_error", "jf_status_str", "jf_abi_version")
+           "jf_gelu_bwd_i8", "jf_add_i8", "jf_layernorm_i8", "jf_quant_error", "jf_status_str",
+           "jf_abi_version")
 
 
 class JetfireError(RuntimeError):
@@ -53,6 +54,11 @@ def _load() -> ctypes.CDLL:
     lib.jf_gelu_i8.restype = cint
     lib.jf_gelu_bwd_i8.argtypes = [ptr, i64, ptr, ptr, i64, ptr, i64, i64, ptr, i64, ptr, ptr]
     lib.jf_gelu_bwd_i8.restype = cint
+    lib.jf_add_i8.argtypes = [ptr, i64, ptr, ptr, i64, ptr, i64, i64, ptr, i64, ptr, ptr]
+    lib.jf_add_i8.restype = cint
+    lib.jf_layernorm_i8.argtypes = [ptr, i64, ptr, i64, i64, ptr, ptr, ctypes.c_float, ptr, i64, ptr, ptr, ptr,
+                                    ptr]
+    lib.jf_layernorm_i8.restype = cint
     lib.jf_quant_error.argtypes = [ptr, i64, i64, i64, cint, ptr, ptr, ptr]
     lib.jf_quant_error.restype = cint
     lib.jf_status_str.argtypes = [cint]
@@ -206,6 +212,47 @@ def gelu_bwd_i8(qdy: torch.Tensor, sdy: torch.Tensor, qx: torch.Tensor, sx: torc
     _check(lib.jf_gelu_bwd_i8(_ptr(qdy), lddy, _ptr(sdy), _ptr(qx), ldx, _ptr(sx), R, C, _ptr(qo), ldo, _ptr(so),
                               _stream(qx.device)), "jf_gelu_bwd_i8")
     return qo, so
+
+
+def add_i8(qa: torch.Tensor, sa: torch.Tensor, qb: torch.Tensor, sb: torch.Tensor,
+           qo: torch.Tensor | None = None, so: torch.Tensor | None = None):
+    """jf_add_i8: residual add of two per-block INT8 tensors, requantized per block."""
+    lda, ldb = _mat(qa, "qa"), _mat(qb, "qb")
+    if qa.dtype != torch.int8 or qb.dtype != torch.int8:
+        raise ValueError("qa and qb must be int8")
+    if qa.shape != qb.shape:
+        raise ValueError("qa and qb must have the same shape")
+    R, C = qa.shape
+    _scales(sa, R, C, "sa")
+    _scales(sb, R, C, "sb")
+    qo = torch.empty((R, C), dtype=torch.int8, device=qa.device) if qo is None else qo
+    so = torch.empty((R // 32, C // 32), dtype=torch.float32, device=qa.device) if so is None else so
+    ldo = _mat(qo, "qo")
+    _check(lib.jf_add_i8(_ptr(qa), lda, _ptr(sa), _ptr(qb), ldb, _ptr(sb), R, C, _ptr(qo), ldo, _ptr(so),
+                         _stream(qa.device)), "jf_add_i8")
+    return qo, so
+
+
+def layernorm_i8(q: torch.Tensor, s: torch.Tensor, gamma: torch.Tensor, beta: torch.Tensor, eps: float = 1e-5,
+                 qo: torch.Tensor | None = None, so: torch.Tensor | None = None, stats: bool = False):
+    """jf_layernorm_i8: LayerNorm over each row of per-block INT8 codes, INT8 out.
+    Returns (qo, so), or (qo, so, mean, rstd) with float64 row statistics if stats."""
+    ldq = _mat(q, "q")
+    if q.dtype != torch.int8:
+        raise ValueError("q must be int8")
+    R, C = q.shape
+    _scales(s, R, C, "s")
+    for t, n in ((gamma, "gamma"), (beta, "beta")):
+        if t.dtype != torch.float32 or not t.is_cuda or tuple(t.shape) != (C,) or not t.is_contiguous():
+            raise ValueError(f"{n} must be a contiguous float32 device tensor of shape ({C},)")
+    qo = torch.empty((R, C), dtype=torch.int8, device=q.device) if qo is None else qo
+    so = torch.empty((R // 32, C // 32), dtype=torch.float32, device=q.device) if so is None else so
+    ldo = _mat(qo, "qo")
+    mean = torch.empty(R, dtype=torch.float64, device=q.device) if stats else None
+    rstd = torch.empty(R, dtype=torch.float64, device=q.device) if stats else None
+    _check(lib.jf_layernorm_i8(_ptr(q), ldq, _ptr(s), R, C, _ptr(gamma), _ptr(beta), float(eps), _ptr(qo), ldo,
+                               _ptr(so), _ptr(mean), _ptr(rstd), _stream(q.device)), "jf_layernorm_i8")
+    return (qo, so, mean, rstd) if stats else (qo, so)
 
 
 def scale_count(granularity: str, rows: int, cols: int) -> int:

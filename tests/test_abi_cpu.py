@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert jf.abi_version() == 3
+    assert jf.abi_version() == 4
     for st in range(0, 9):
         assert jf.status_str(st) and jf.status_str(st) != "unknown status"
     assert jf.status_str(99) == "unknown status"
@@ -113,6 +113,46 @@ def test_gelu_bwd_validation_codes():
     assert g(dy, 64, sdy, x, 64, sx, 64, 64, P(BASE + 0x20000100), 64, so, None) == jf.JF_ERR_ALIAS
     assert g(dy, 64, sdy, x, 64, sx, 64, 64, qo, 64, sx, None) == jf.JF_ERR_ALIAS
     assert g(dy, 64, sdy, x, 64, sx, 0, 64, qo, 64, so, None) == jf.JF_OK             # empty
+
+
+def test_add_validation_codes():
+    f = jf.lib.jf_add_i8
+    a, sa, b, sb = P(BASE), P(BASE + 0x10000000), P(BASE + 0x20000000), P(BASE + 0x30000000)
+    qo, so = P(BASE + 0x40000000), P(BASE + 0x50000000)
+    assert f(a, 64, sa, None, 64, sb, 64, 64, qo, 64, so, None) == jf.JF_ERR_NULL
+    assert f(a, 64, sa, b, 64, sb, 64, 64, qo, 64, None, None) == jf.JF_ERR_NULL
+    assert f(a, 64, sa, b, 64, sb, 40, 64, qo, 64, so, None) == jf.JF_ERR_SHAPE
+    assert f(a, 64, sa, b, 32, sb, 64, 64, qo, 64, so, None) == jf.JF_ERR_LD
+    assert f(a, 64, sa, b, 64, sb, 64, 64, qo, 68, so, None) == jf.JF_ERR_LD
+    assert f(P(BASE + 8), 64, sa, b, 64, sb, 64, 64, qo, 64, so, None) == jf.JF_ERR_ALIGN
+    assert f(a, 64, sa, b, 64, P(BASE + 0x30000001), 64, 64, qo, 64, so, None) == jf.JF_ERR_ALIGN
+    assert f(a, 64, sa, b, 64, sb, 64, 64, a, 64, so, None) == jf.JF_ERR_ALIAS          # in place
+    assert f(a, 64, sa, b, 64, sb, 64, 64, qo, 64, P(BASE + 0x20000000 + 4032), None) == jf.JF_ERR_ALIAS
+    assert f(a, 64, sa, b, 64, sb, 64, 64, qo, 64, P(BASE + 0x40000000 + 4080), None) == jf.JF_ERR_ALIAS
+    assert f(a, 64, sa, b, 64, sb, 0, 64, None, 64, None, None) == jf.JF_OK                # empty
+
+
+def test_layernorm_validation_codes():
+    f = jf.lib.jf_layernorm_i8
+    q, s, g, b = P(BASE), P(BASE + 0x10000000), P(BASE + 0x20000000), P(BASE + 0x30000000)
+    qo, so, m, r = P(BASE + 0x40000000), P(BASE + 0x50000000), P(BASE + 0x60000000), P(BASE + 0x70000000)
+
+    def ln(q=q, ldq=64, s=s, rows=64, cols=64, g=g, b=b, eps=1e-5, qo=qo, ldo=64, so=so, m=m, r=r):
+        return f(q, ldq, s, rows, cols, g, b, eps, qo, ldo, so, m, r, None)
+
+    assert ln(g=None) == jf.JF_ERR_NULL
+    assert ln(so=None) == jf.JF_ERR_NULL
+    assert ln(cols=80) == jf.JF_ERR_SHAPE
+    assert ln(ldq=48) == jf.JF_ERR_LD
+    assert ln(b=P(BASE + 0x30000004)) == jf.JF_ERR_ALIGN                  # beta is read 16 bytes at a time
+    assert ln(m=P(BASE + 0x60000004)) == jf.JF_ERR_ALIGN
+    assert ln(eps=-1e-6) == jf.JF_ERR_ARG
+    assert ln(eps=float("inf")) == jf.JF_ERR_ARG
+    assert ln(eps=float("nan")) == jf.JF_ERR_ARG
+    assert ln(qo=q) == jf.JF_ERR_ALIAS
+    assert ln(m=P(BASE + 0x20000000 + 128)) == jf.JF_ERR_ALIAS             # mean over gamma
+    assert ln(r=P(BASE + 0x60000000 + 256)) == jf.JF_ERR_ALIAS             # rstd over mean
+    assert ln(rows=0, q=None, s=None, qo=None, so=None) == jf.JF_OK
 
 
 def test_quant_error_validation_codes():
