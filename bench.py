@@ -306,6 +306,124 @@ def quant_error_section(step, reps=10):
     return res
 
 
+def _time_us(fn, reps):
+    import torch
+
+    fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps * 1e3
+
+
+def data_flow_ops_section(step, reps=20):
+    """The residual add and LayerNorm (INT8 in and out) on the step's shapes:
+    R = X + A (8192 x 4096), then LayerNorm of R over the hidden dimension."""
+    import numpy as np
+    import torch
+
+    jf = step.jf
+    qx, sx = step.q["X"]
+    qa, sa = step.q["A"]
+    dev = qx.device
+    jf.quantize_block(step.fp["X"], q=qx, s=sx)
+    jf.requant_block(step.fp["A"], q=qa, s=sa)
+    qr, sr = torch.empty_like(qx), torch.empty_like(sx)
+    ql, sl = torch.empty_like(qx), torch.empty_like(sx)
+    g = np.random.default_rng(11)
+    C = qx.shape[1]
+    gamma = torch.from_numpy(g.normal(1.0, 0.1, C).astype(np.float32)).to(dev)
+    beta = torch.from_numpy(g.normal(0.0, 0.1, C).astype(np.float32)).to(dev)
+    n = qx.numel()
+    add_us = _time_us(lambda: jf.add_i8(qx, sx, qa, sa, qr, sr), reps)
+    ln_us = _time_us(lambda: jf.layernorm_i8(qr, sr, gamma, beta, 1e-5, ql, sl), reps)
+    nblk = n // 1024
+    return {"residual_add": {"us": round(add_us, 1), "gbs": round((3 * n + 12 * nblk) / (add_us * 1e-6) / 1e9, 1),
+                             "bytes_per_element": 3.0117},
+            "layernorm": {"us": round(ln_us, 1), "gbs": round((2 * n + 8 * nblk) / (ln_us * 1e-6) / 1e9, 1),
+                          "bytes_per_element": 2.0078},
+            "what": "R = X + A and LayerNorm(R) on 8192x4096 per-block INT8 tensors (INT8 in and out)"}
+
+
+def mlp1024_section(reps=10):
+    """The GPT2-medium-like MLP (8192 tokens, 1024 -> 4096 -> 1024) in the
+    INT8 data flow (quantize X, W1, W2, dY; FC1 -> GELU -> FC2; FC2 dgrad and
+    wgrad; GELU backward; FC1 dgrad and wgrad: 13 kernels) against its six
+    GEMM shapes as bfloat16 torch.mm."""
+    import torch
+
+    from int8_block_quantized_amd import inputs
+    from int8_block_quantized_amd import jetfire as jf
+
+    dev = torch.device("cuda:0")
+    wl = inputs.gpt2_medium_mlp()
+    fp = {n: torch.from_numpy(wl.make(n)).to(dev) for n in ("X", "W1", "W2", "dY2")}
+    T = 8192
+
+    def buf(r, c):
+        return (torch.empty((r, c), dtype=torch.int8, device=dev),
+                torch.empty((r // 32, c // 32), dtype=torch.float32, device=dev))
+
+    q = {n: buf(*t.shape) for n, t in fp.items()}
+    for n, (r, c) in {"H": (T, 4096), "G": (T, 4096), "Y": (T, 1024), "dG": (T, 4096), "dW2": (4096, 1024),
+                      "dH": (T, 4096), "dX": (T, 1024), "dW1": (1024, 4096)}.items():
+        q[n] = buf(r, c)
+
+    def gemm(a, b, ta, tb, c):
+        jf.gemm_i8_blockscaled(q[a][0], q[a][1], q[b][0], q[b][1], ta, tb, out="i8", c=q[c][0], sc=q[c][1])
+
+    gemms = [("X", "W1", 0, 0, "H"), ("G", "W2", 0, 0, "Y"), ("dY2", "W2", 0, 1, "dG"), ("G", "dY2", 1, 0, "dW2"),
+             ("dH", "W1", 0, 1, "dX"), ("X", "dH", 1, 0, "dW1")]
+
+    def step():
+        for n in ("X", "W1", "W2"):
+            jf.quantize_block(fp[n], q=q[n][0], s=q[n][1])
+        gemm(*gemms[0])
+        jf.gelu_i8(q["H"][0], q["H"][1], qo=q["G"][0], so=q["G"][1])
+        gemm(*gemms[1])
+        jf.quantize_block(fp["dY2"], q=q["dY2"][0], s=q["dY2"][1])
+        gemm(*gemms[2])
+        gemm(*gemms[3])
+        jf.gelu_bwd_i8(q["dG"][0], q["dG"][1], q["H"][0], q["H"][1], qo=q["dH"][0], so=q["dH"][1])
+        gemm(*gemms[4])
+        gemm(*gemms[5])
+
+    def gemms_only():
+        for gm in gemms:
+            gemm(*gm)
+
+    ops = wl.gemm_ops()
+    step_us = _time_us(step, reps)
+    gemm_us = _time_us(gemms_only, reps)
+    g = torch.Generator(device=dev)
+    g.manual_seed(8)
+    mats = []
+    for a, b, ta, tb, c in gemms:
+        M, N = q[c][0].shape
+        K = q[a][0].shape[0] if ta else q[a][0].shape[1]
+        mats.append((torch.randn((M, K), device=dev, generator=g).to(torch.bfloat16),
+                     torch.randn((K, N), device=dev, generator=g).to(torch.bfloat16),
+                     torch.empty((M, N), device=dev, dtype=torch.bfloat16)))
+
+    def bf16():
+        for A, B, C in mats:
+            torch.mm(A, B, out=C)
+
+    bf_us = _time_us(bf16, reps)
+    del mats, q, fp
+    torch.cuda.empty_cache()
+    return {"int8_step_ms": round(step_us / 1e3, 4), "int8_step_tops": round(ops / (step_us * 1e-6) / 1e12, 1),
+            "int8_gemm_ms": round(gemm_us / 1e3, 4), "int8_gemm_tops": round(ops / (gemm_us * 1e-6) / 1e12, 1),
+            "bf16_gemm_ms": round(bf_us / 1e3, 4), "bf16_tflops": round(ops / (bf_us * 1e-6) / 1e12, 1),
+            "int8_gemm_speedup": round(bf_us / gemm_us, 3), "gemm_ops": ops,
+            "what": "GPT2-medium-like MLP, 8192 tokens, 1024->4096->1024: INT8 data flow (13 kernels) and its "
+                    "6 INT8 GEMMs vs the same 6 GEMM shapes as torch.mm in bfloat16"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -405,6 +523,9 @@ def main():
                         "bf16 outputs; compared with the INT8 GEMMs' time in the step"}
 
     qerr = quant_error_section(step)
+    dfo = data_flow_ops_section(step)
+
+    mlp1024 = mlp1024_section() if args.bf16_steps > 0 else None
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -437,6 +558,8 @@ def main():
         "cpu_baseline": cpu,
         "bf16_reference": bf16,
         "quant_error": qerr,
+        "data_flow_ops": dfo,
+        "mlp_hidden1024": mlp1024,
         "kernels": kernels,
         "host_wall_s": round(wall, 3),
     }

@@ -69,6 +69,26 @@
 #ifndef JF_GEMM_PIPE
 #define JF_GEMM_PIPE 0
 #endif
+// Smaller tile for grids that would leave SIMDs with one wavefront or none:
+// used when the main tile gives fewer than JF_GEMM_SMALL_BELOW workgroups.
+// One 32x32 block per wavefront (64x128 tile, eight wavefronts) quadruples
+// the wavefronts of such a grid; with one wavefront per SIMD the per-k-block
+// rescale issues about 2.6x slower than with four.
+#ifndef JF_GEMM_SMALL_WM
+#define JF_GEMM_SMALL_WM 1
+#endif
+#ifndef JF_GEMM_SMALL_WN
+#define JF_GEMM_SMALL_WN 1
+#endif
+#ifndef JF_GEMM_SMALL_GM
+#define JF_GEMM_SMALL_GM 2
+#endif
+#ifndef JF_GEMM_SMALL_GN
+#define JF_GEMM_SMALL_GN 4
+#endif
+#ifndef JF_GEMM_SMALL_BELOW
+#define JF_GEMM_SMALL_BELOW 512
+#endif
 #ifndef JF_GEMM_WAVES_PER_EU
 #define JF_GEMM_WAVES_PER_EU 4
 #endif
@@ -470,11 +490,10 @@ hipError_t launch_cfg(int64_t M, int64_t N, int64_t K, const int8_t *A, int64_t 
     return hipGetLastError();
 }
 
-template <int GM, int GN, int KB, int S, bool A_KC, bool B_KC, bool OUT_I8>
+template <int WM, int WN, int GM, int GN, int KB, int S, bool A_KC, bool B_KC, bool OUT_I8>
 hipError_t dispatch_narrow(int64_t M, int64_t N, int64_t K, const int8_t *A, int64_t lda, const float *sA,
                            const int8_t *B, int64_t ldb, const float *sB, void *C, int64_t ldc, float *sC,
                            hipStream_t stream) {
-    constexpr int WM = JF_GEMM_WM, WN = JF_GEMM_WN;
     // Per-lane load offsets stay below (tile edge) * ld + tile edge; below
     // 2^31 they go in one 32-bit VGPR beside a scalar base.
     constexpr int64_t kEdge = std::max({GM * WM * kBlock, GN * WN * kBlock, KB * kBlock});
@@ -494,10 +513,18 @@ hipError_t dispatch_kb(int64_t M, int64_t N, int64_t K, const int8_t *A, int64_t
     // 32-byte ones load much worse when an operand is k-contiguous) in a
     // two-deep ring, which leaves LDS for four wavefronts per SIMD.  A stage
     // must lie inside K; odd K/32 falls back to one k-block per stage.
-    if ((K / kBlock) % JF_GEMM_KB == 0)
-        return dispatch_narrow<JF_GEMM_GM, JF_GEMM_GN, JF_GEMM_KB, JF_GEMM_S, A_KC, B_KC, OUT_I8>(
-            M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC, stream);
-    return dispatch_narrow<2, 2, 1, 4, A_KC, B_KC, OUT_I8>(M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC, stream);
+    // Grids of fewer than JF_GEMM_SMALL_BELOW main tiles take the smaller tile
+    // (the per-element k order, and so every result bit, is the same).
+    if ((K / kBlock) % JF_GEMM_KB != 0)
+        return dispatch_narrow<JF_GEMM_WM, JF_GEMM_WN, 2, 2, 1, 4, A_KC, B_KC, OUT_I8>(M, N, K, A, lda, sA, B, ldb,
+                                                                                 sB, C, ldc, sC, stream);
+    constexpr int64_t BM = JF_GEMM_GM * JF_GEMM_WM * kBlock, BN = JF_GEMM_GN * JF_GEMM_WN * kBlock;
+    const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    if (tiles < JF_GEMM_SMALL_BELOW)
+        return dispatch_narrow<JF_GEMM_SMALL_WM, JF_GEMM_SMALL_WN, JF_GEMM_SMALL_GM, JF_GEMM_SMALL_GN, JF_GEMM_KB,
+                               JF_GEMM_S, A_KC, B_KC, OUT_I8>(M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC, stream);
+    return dispatch_narrow<JF_GEMM_WM, JF_GEMM_WN, JF_GEMM_GM, JF_GEMM_GN, JF_GEMM_KB, JF_GEMM_S, A_KC, B_KC, OUT_I8>(
+        M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC, stream);
 }
 
 template <bool A_KC, bool B_KC>
