@@ -44,6 +44,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="target CPU time of the oracle baseline sample (0 disables it)")
+    p.add_argument("--extras", type=int, default=1,
+                   help="1: after the timed step also measure the quantization-error harness, residual add, "
+                        "LayerNorm and the hidden-1024 MLP; 0: the step only")
     p.add_argument("--bf16-steps", type=int, default=5,
                    help="steps of the bf16 reference (the same 12 GEMMs with torch.mm in bfloat16; 0 skips it)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -522,10 +525,10 @@ def main():
                 "what": "the 12 GEMM shapes as torch.mm in bfloat16 (vendor BLAS), operands pre-laid-out, "
                         "bf16 outputs; compared with the INT8 GEMMs' time in the step"}
 
-    qerr = quant_error_section(step)
-    dfo = data_flow_ops_section(step)
+    qerr = quant_error_section(step) if args.extras else None
+    dfo = data_flow_ops_section(step) if args.extras else None
 
-    mlp1024 = mlp1024_section() if args.bf16_steps > 0 else None
+    mlp1024 = mlp1024_section() if args.extras else None
 
     cpu = None
     if args.cpu_seconds > 0:
