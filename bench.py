@@ -427,6 +427,49 @@ def mlp1024_section(reps=10):
                     "6 INT8 GEMMs vs the same 6 GEMM shapes as torch.mm in bfloat16"}
 
 
+def memory_bound_section(reps=20):
+    """The memory-bound workload: a 16384 x 16384 fp32 activation (N(0,1),
+    1% of columns x100) through jf_quantize_block, then jf_gelu_i8 on its codes.
+    Two copies of every input are used in turn so no call finds its input in
+    the 256 MB Infinity Cache.  Algorithmic bytes per element: quantize 4 + 1
+    + 4/1024, GELU 1 + 1 + 8/1024."""
+    import torch
+
+    from int8_block_quantized_amd import inputs
+    from int8_block_quantized_amd import jetfire as jf
+
+    dev = torch.device("cuda:0")
+    x = torch.from_numpy(inputs.memory_bound().make("X")).to(dev)
+    xs = [x, x.clone()]
+    R, C = x.shape
+    n = R * C
+    qs = [jf.quantize_block(t) for t in xs]
+    q, s = torch.empty_like(qs[0][0]), torch.empty_like(qs[0][1])
+    qo, so = torch.empty_like(q), torch.empty_like(s)
+    i = [0]
+
+    def quant():
+        i[0] ^= 1
+        jf.quantize_block(xs[i[0]], q=q, s=s)
+
+    def gelu():
+        i[0] ^= 1
+        jf.gelu_i8(qs[i[0]][0], qs[i[0]][1], qo=qo, so=so)
+
+    q_us = _time_us(quant, reps)
+    g_us = _time_us(gelu, reps)
+    qb, gb = n * (5 + 4 / 1024), n * (2 + 8 / 1024)
+    del xs, x, qs
+    torch.cuda.empty_cache()
+    out = {}
+    for name, us, nb in (("quantize", q_us, qb), ("gelu", g_us, gb)):
+        gbs = nb / (us * 1e-6) / 1e9
+        out[name] = {"us": round(us, 1), "gbs": round(gbs, 1), "frac_of_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+    out["what"] = ("16384x16384 fp32 N(0,1) with 1% of columns x100: jf_quantize_block (fp32 -> INT8 + 32x32 "
+                   "scales), then jf_gelu_i8 on the codes; two input copies used in turn")
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -529,6 +572,7 @@ def main():
     dfo = data_flow_ops_section(step) if args.extras else None
 
     mlp1024 = mlp1024_section() if args.extras else None
+    membound = memory_bound_section() if args.extras else None
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -563,6 +607,7 @@ def main():
         "quant_error": qerr,
         "data_flow_ops": dfo,
         "mlp_hidden1024": mlp1024,
+        "memory_bound": membound,
         "kernels": kernels,
         "host_wall_s": round(wall, 3),
     }

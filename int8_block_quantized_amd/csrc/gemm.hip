@@ -37,8 +37,8 @@
 // Workgroup: GM x GN wavefronts; wavefront tile WM x WN output blocks; LDS
 // stages of KB k-blocks in an S-deep ring.  Defaults: 2 x 4 wavefronts of
 // 2 x 2 blocks (a 128 x 256 tile), stages of two k-blocks, a two-deep ring,
-// each MFMA followed by its own rescale (PIPE 0), about 110 VGPRs: four
-// wavefronts per SIMD.  The rescale is VALU work (two instructions per
+// the stage's fragments read up front, each MFMA followed by its own rescale
+// (PIPE 0), about 125 VGPRs: four wavefronts per SIMD.  The rescale is VALU work (two instructions per
 // element and k-block) and the VALU issue rate of one wavefront is far below
 // the SIMD's, so occupancy, not MFMA scheduling, sets the pace.
 #include <algorithm>
@@ -407,23 +407,24 @@ __global__ __launch_bounds__(64 * GM * GN) JF_GEMM_OCCUPANCY void k_gemm_i8bs(
                 if (t + 1 < T) pc = pn;
             }
         } else {
-            // One k-block at a time, each MFMA followed by its rescale: fewer
-            // live registers (more wavefronts per SIMD hide the latencies).
+            // Every k-block's fragments and scale products of the stage are
+            // read first (the later k-blocks' LDS reads overlap the first
+            // k-block's MFMAs), then each MFMA is followed by its rescale.
+            v4i af[KB][WM], bf[KB][WN];
+            float sg[KB][WM][WN];
 #pragma unroll
-            for (int kk = 0; kk < KB; ++kk) {
-                v4i af[WM], bf[WN];
-                float sg[WM][WN];
-                load_kk(kk, af, bf, sg);
-                if (kk == 0 && st + S - 1 < nstage) issue(std::integral_constant<int, (SLOT + S - 1) % S>{});
+            for (int kk = 0; kk < KB; ++kk) load_kk(kk, af[kk], bf[kk], sg[kk]);
+            if (st + S - 1 < nstage) issue(std::integral_constant<int, (SLOT + S - 1) % S>{});
+#pragma unroll
+            for (int kk = 0; kk < KB; ++kk)
 #pragma unroll
                 for (int a = 0; a < WM; ++a)
 #pragma unroll
                     for (int b = 0; b < WN; ++b) {
-                        const v16i p = __builtin_amdgcn_mfma_i32_32x32x32_i8(bf[b], af[a], v16i{}, 0, 0, 0);
-                        rescale(acc[a][b], sg[a][b], p);
+                        const v16i p = __builtin_amdgcn_mfma_i32_32x32x32_i8(bf[kk][b], af[kk][a], v16i{}, 0, 0, 0);
+                        rescale(acc[a][b], sg[kk][a][b], p);
                         __builtin_amdgcn_sched_barrier(0);
                     }
-            }
         }
     };
     for (int st0 = 0; st0 < nstage; st0 += S) {
