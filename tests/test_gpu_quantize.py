@@ -3,7 +3,9 @@
 Bar: codes and scales bit-exact (the rule's decisions are binary32 on both
 sides).  Cases: the tiny 256x256 workload, a ragged shape, bfloat16 input,
 strided (ld > cols) views, edge blocks (zero, underflow, subnormal scale,
-exact ties, +-max), and the 16384 x 16384 memory-bound workload in full.
+exact ties, +-max), several row segments per band with a ragged last one,
+a grid split over several launches (2^20 + 64 rows), and the 16384 x 16384
+memory-bound workload in full.
 """
 import numpy as np
 import pytest
@@ -95,6 +97,36 @@ def test_memory_bound_workload_full():
     q, s = jf.quantize_block(dev(x))
     qh, sh = host(q), host(s)
     note("memory-bound: oracle")
+    oq, os_ = oracle.quantize(x)
+    np.testing.assert_array_equal(sh, os_)
+    np.testing.assert_array_equal(qh, oq)
+
+
+@pytest.mark.parametrize("rows,cols,dtype", [(320, 800, "f32"), (96, 1056, "bf16"), (64, 2080, "f32")])
+def test_several_row_segments_ragged(rows, cols, dtype):
+    """Several 1 KiB row segments per 32-row band with a partial last one
+    (fp32: 8 blocks per segment, bfloat16: 16)."""
+    x = inputs.activation(204, cols, rows, cols, n_outlier_cols=max(1, cols // 100), factor=80.0)
+    if dtype == "bf16":
+        xt = torch.from_numpy(x).to(torch.bfloat16)
+        q, s = jf.quantize_block(xt.to(DEV))
+        oq, os_ = oracle.quantize(xt.view(torch.int16).numpy().view(np.uint16))
+    else:
+        q, s = jf.quantize_block(dev(x))
+        oq, os_ = oracle.quantize(x)
+    np.testing.assert_array_equal(host(s), os_)
+    np.testing.assert_array_equal(host(q), oq)
+
+
+def test_more_bands_than_one_launch_holds():
+    """2^20 + 64 rows: more 32-row bands than one launch's grid dimension
+    takes (2^15), so the launcher splits the grid; the band index must carry
+    across the launches."""
+    rows, cols = (1 << 20) + 64, 64
+    note(f"quantize {rows}x{cols}: generating")
+    x = inputs.activation(205, 0, rows, cols, n_outlier_cols=1, factor=60.0)
+    q, s = jf.quantize_block(dev(x))
+    qh, sh = host(q), host(s)
     oq, os_ = oracle.quantize(x)
     np.testing.assert_array_equal(sh, os_)
     np.testing.assert_array_equal(qh, oq)
