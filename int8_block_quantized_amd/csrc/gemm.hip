@@ -217,23 +217,39 @@ struct DTile {
     }
 };
 
-// Codes of the 16 values of a lane under one non-zero block scale, with no
-// branch: the reciprocal-product candidate is replaced by the IEEE-quotient
-// code wherever it lies within 2^-15 of a half-integer (see quant_codes for
-// the bound).  Straight-line code keeps the epilogue's register demand at the
-// main loop's level; the 16 divisions cost a few percent of a tile.
-__device__ __forceinline__ void quant_codes_straight(const float (&x)[16], float s, int (&code)[16]) {
+// Codes of the 16 values of a lane under one non-zero block scale.  The
+// reciprocal-product candidate rne(x * fl(1/s)) is the reference code unless
+// x * fl(1/s) lies within 2^-15 of a half-integer (see quant_codes for the
+// bound); those values (about 6 in 10^5, or all of them when 1/s overflows)
+// are redone with the IEEE quotient, one per lane and pass of a loop whose
+// trip count is wave-uniform and almost always zero.  The element is picked
+// and put back by selects, so the loop adds no register pressure to the
+// main loop's level.
+__device__ __forceinline__ void quant_codes_rare(const float (&x)[16], float s, int (&code)[16]) {
     const float r = 1.0f / s;
     const bool finite_r = r < __builtin_inff();
+    float n[16];
+    uint32_t near = 0;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
         const float t = x[e] * r;
-        float n = __builtin_rintf(t);
-        const float qd = __builtin_rintf(x[e] / s);
-        if (!finite_r || fabsf(t - n) > 0.5f - 0x1p-15f) n = qd;
-        code[e] = (int)fminf(fmaxf(n, -127.0f), 127.0f);
-        __builtin_amdgcn_sched_barrier(0);
+        n[e] = __builtin_rintf(t);
+        if (!finite_r || fabsf(t - n[e]) > 0.5f - 0x1p-15f) near |= 1u << e;
     }
+    while (__builtin_amdgcn_ballot_w64(near != 0) != 0) {
+        if (near != 0) {
+            const int k = __builtin_ctz(near);
+            near &= near - 1;
+            float xk = x[0];
+#pragma unroll
+            for (int e = 1; e < 16; ++e) xk = k == e ? x[e] : xk;
+            const float q = __builtin_rintf(xk / s);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) n[e] = k == e ? q : n[e];
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) code[e] = (int)fminf(fmaxf(n[e], -127.0f), 127.0f);
 }
 
 template <int WM, int WN, int GM, int GN, int KB, int S, bool A_KC, bool B_KC, bool OUT_I8, bool NARROW>
@@ -460,7 +476,7 @@ __global__ __launch_bounds__(64 * GM * GN) JF_GEMM_OCCUPANCY void k_gemm_i8bs(
                 int code[16];
 #pragma unroll
                 for (int r = 0; r < 16; ++r) code[r] = 0;
-                if (sc != 0.0f) quant_codes_straight(acc[a][b], sc, code);
+                if (sc != 0.0f) quant_codes_rare(acc[a][b], sc, code);
                 int8_t *C = reinterpret_cast<int8_t *>(Cv);
 #pragma unroll
                 for (int g = 0; g < 4; ++g)

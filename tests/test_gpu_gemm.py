@@ -200,3 +200,38 @@ def test_gpt2_base_linear_full_size():
 
 def test_hidden4096_block_full_size():
     check_workload_gemms(inputs.hidden4096_block(), 12, f32_labels=("qkv.fwd", "fc2.wgrad"))
+
+
+@pytest.mark.parametrize("ta,tb", COMBOS)
+@pytest.mark.parametrize("scale", [1.0, 1e-20])
+def test_requant_epilogue_ties_and_tiny_scales(ta, tb, scale):
+    """INT8 output where the codes sit exactly on half-integers: every column
+    of B holds two ones, so acc = a + a' (an integer, |acc| <= 254) and each
+    output block's maximum is 254, so s = 2 and every odd acc is a tie that
+    only the IEEE quotient decides (round half to even).  With scales of
+    1e-20 the products are subnormal and fl(1/s) overflows, so every element
+    takes the quotient path.  Codes and scales must match the oracle
+    exactly."""
+    M, N, K = 64, 96, 64
+    g = np.random.default_rng(77)
+    A = g.integers(-127, 128, size=(M, K)).astype(np.int8)
+    B = np.zeros((K, N), np.int8)
+    t1 = g.integers(0, K, size=N)
+    t2 = (t1 + 1 + g.integers(0, K - 1, size=N)) % K
+    B[t1, np.arange(N)] = 1
+    B[t2, np.arange(N)] = 1
+    for I in range(M // 32):
+        for J in range(N // 32):
+            A[32 * I, t1[32 * J]] = 127
+            A[32 * I, t2[32 * J]] = 127
+    sA = np.full((M // 32, K // 32), scale, np.float32)
+    sB = np.full((K // 32, N // 32), scale, np.float32)
+    As, sAs, Bs, sBs = stored(A, ta), stored(sA, ta), stored(B, tb), stored(sB, tb)
+    q, s = jf.gemm_i8_blockscaled(dev(As), dev(sAs), dev(Bs), dev(sBs), ta, tb, out="i8")
+    oq, os_ = oracle.gemm_i8(As, sAs, Bs, sBs, ta=ta, tb=tb)
+    np.testing.assert_array_equal(host(s), os_)
+    np.testing.assert_array_equal(host(q), oq)
+    if scale == 1.0:
+        assert np.all(os_ == 2.0)
+        acc = A.astype(np.int64) @ B.astype(np.int64)
+        assert (acc % 2 != 0).mean() > 0.3, "too few ties to exercise the rule"
