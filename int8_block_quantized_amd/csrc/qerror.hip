@@ -7,99 +7,131 @@
 // on four group shapes: 32x32 block, token (row), channel (column), tensor;
 // returns the group scales and sum (x - fl(s*q))^2 in binary64.
 //
-// 32x32 blocks take one pass (a wavefront holds its blocks whole).  Rows,
-// columns and the tensor take three launches after clearing: group maxima
-// (non-negative binary32 maxima combined as bit patterns with atomic integer
-// max), maxima -> scales, then codes and errors.  Error sums are per-lane
-// binary64, reduced per workgroup, one atomic add each.  The
-// element mapping is the quantize kernel's: a wavefront takes four
-// horizontally adjacent blocks, lane l holding rows 2i + l/32 (i = 0..15)
-// and elements 4(l%32)..4(l%32)+3 of the 128-element group row.
+// 32x32 blocks take one pass.  Rows, columns and the tensor take three
+// launches after clearing: group maxima (non-negative binary32 maxima
+// combined as bit patterns with atomic integer max), maxima -> scales, then
+// codes and errors.  Error sums are per-lane binary64, reduced per
+// workgroup, one atomic add each.
+//
+// Element mapping: the quantizer's band workgroup.  A workgroup covers one
+// 32-row band of blocks and a 1 KiB segment (256 columns, 8 blocks) of each
+// row; its four wavefronts hold eight rows each, lane l the four values at
+// columns 4l..4l+3 of the segment (block l/8), so every load reads a whole
+// 1 KiB row segment.
+#include <algorithm>
+
 #include "jf_device.h"
 #include "jf_launch.h"
 
 namespace jf {
 namespace {
 
-constexpr int kGroup = 4;
+constexpr int kRows = 8;                    // rows per wavefront
+constexpr int kWaves = kBlock / kRows;      // 4 wavefronts
+constexpr int kSegBlocks = 8;               // blocks per 1 KiB segment of fp32
+constexpr int kMaxSegPerWG = 8;   // segments per workgroup, in turn (at most)
+constexpr int64_t kMaxGridX = 1 << 20, kMaxGridY = 1 << 15;
 
 enum { kBlockG = 0, kToken = 1, kChannel = 2, kTensor = 3 };
 
 struct Tile {
-    float v[16][4];
-    int64_t gi, row0, col0;   // block row, first row, first column of the lane's 4 elements
-    int gj0;                  // first block column of the group
-    bool valid;               // the lane's block exists (tail groups)
+    float v[kRows][4];
+    int64_t row0, col0;   // first row and first column of the lane's values
+    int bj;               // block column of the lane (clamped)
+    bool valid;           // the lane's block exists (ragged last segment)
 };
 
-__device__ __forceinline__ Tile load_tile(const float *x, int64_t ldx, int nbc, int ngc, int64_t grp) {
+__device__ __forceinline__ Tile load_tile(const float *x, int64_t ldx, int nbc, int seg, int band) {
     Tile t;
-    const int lane = threadIdx.x & (kWave - 1);
-    t.gi = grp / ngc;
-    t.gj0 = (int)(grp - t.gi * ngc) * kGroup;
-    const int b = (lane & 31) >> 3;
-    const int bj = min(t.gj0 + b, nbc - 1);
-    t.valid = t.gj0 + b < nbc;
-    t.row0 = t.gi * kBlock + (lane >> 5);
-    t.col0 = (int64_t)bj * kBlock + 4 * (lane & 7);
+    const int lane = threadIdx.x & (kWave - 1), wave = wave_id_uniform();
+    const int bj = seg * kSegBlocks + lane / 8;
+    t.valid = bj < nbc;
+    t.bj = min(bj, nbc - 1);
+    t.row0 = (int64_t)band * kBlock + wave * kRows;
+    t.col0 = (int64_t)t.bj * kBlock + 4 * (lane & 7);
     const float *src = x + t.row0 * ldx + t.col0;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const f32x4 f = *reinterpret_cast<const f32x4 *>(src + 2 * i * ldx);
+    for (int i = 0; i < kRows; ++i) {
+        const f32x4 f = *reinterpret_cast<const f32x4 *>(src + i * ldx);
         t.v[i][0] = f.x; t.v[i][1] = f.y; t.v[i][2] = f.z; t.v[i][3] = f.w;
     }
     return t;
 }
 
-// Row, column or tensor maxima as uint32 bit patterns (x >= 0: IEEE order =
-// unsigned order), combined with atomic max.
-template <int G>
-__global__ __launch_bounds__(256) void k_qe_max(const float *__restrict__ x, int64_t ldx, int nbc, int ngc,
-                                                int64_t ngroups, uint32_t *__restrict__ mx) {
-    __shared__ uint32_t wg_max[4];
+// Sum of a binary64 value over the workgroup, then one atomic add.
+__device__ __forceinline__ void wg_sum_add(double acc, double *sse) {
+    __shared__ double wg_sum[kWaves];
     const int lane = threadIdx.x & (kWave - 1), wave = wave_id_uniform();
-    const int64_t grp_raw = (int64_t)blockIdx.x * 4 + wave;
-    const Tile t = load_tile(x, ldx, nbc, ngc, min(grp_raw, ngroups - 1));
-    const bool live = grp_raw < ngroups && t.valid;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+    if (lane == 0) wg_sum[wave] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) atomicAdd(sse, (wg_sum[0] + wg_sum[1]) + (wg_sum[2] + wg_sum[3]));
+}
+
+// Row, column or tensor maxima as uint32 bit patterns (x >= 0: IEEE order =
+// unsigned order), combined with atomic max.  A workgroup takes spw (up to
+// eight) segments of its band in turn, the next one's loads issued before
+// the current one is reduced: every workgroup ends in atomics, and those on
+// one address (the tensor maximum, the error sum) serialize in L2 at roughly
+// one per 13 ns (the one-segment workgroups of a 16384 x 16384 input spent
+// most of their time there), so fewer, longer workgroups keep them off the
+// critical path; the launcher keeps at least 1024 workgroups.
+template <int G>
+__global__ __launch_bounds__(64 * kWaves) void k_qe_max(const float *__restrict__ x, int64_t ldx, int nbc, int nseg,
+                                                        int spw, int sg0, int band0, uint32_t *__restrict__ mx) {
+    __shared__ uint32_t wmax[2][kWaves][kWave * 4];
+    const int lane = threadIdx.x & (kWave - 1), wave = wave_id_uniform();
+    const int band = band0 + blockIdx.y, seg_first = (sg0 + blockIdx.x) * spw;
+    float tmax = 0.0f;                                   // tensor: running maximum
+    Tile t = load_tile(x, ldx, nbc, min(seg_first, nseg - 1), band);
+#pragma unroll 1
+    for (int j = 0; j < spw && seg_first + j < nseg; ++j) {
+        const Tile nt = load_tile(x, ldx, nbc, min(seg_first + j + 1, nseg - 1), band);   // prefetch
+        if constexpr (G == kTensor) {
+#pragma unroll
+            for (int i = 0; i < kRows; ++i)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) tmax = fmaxf(tmax, t.valid ? fabsf(t.v[i][e]) : 0.0f);
+        } else if constexpr (G == kToken) {
+            // row i of the wavefront: max over the lane's 4 values, then the wavefront
+#pragma unroll
+            for (int i = 0; i < kRows; ++i) {
+                float m = 0.0f;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) m = fmaxf(m, fabsf(t.v[i][e]));
+                const uint32_t u = __float_as_uint(wave_max_nonneg(t.valid ? m : 0.0f));
+                if (lane == 0) atomicMax(mx + t.row0 + i, u);
+            }
+        } else {
+            // columns col0..col0+3: max over the wavefront's 8 rows, then over
+            // the four wavefronts through LDS (two buffers: one barrier per
+            // segment), one atomic per column
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float m = 0.0f;
+#pragma unroll
+                for (int i = 0; i < kRows; ++i) m = fmaxf(m, fabsf(t.v[i][e]));
+                wmax[j & 1][wave][4 * lane + e] = __float_as_uint(m);
+            }
+            __syncthreads();
+            if (wave == 0 && t.valid) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int c = 4 * lane + e;
+                    atomicMax(mx + t.col0 + e, max(max(wmax[j & 1][0][c], wmax[j & 1][1][c]),
+                                                   max(wmax[j & 1][2][c], wmax[j & 1][3][c])));
+                }
+            }
+        }
+        t = nt;
+    }
     if constexpr (G == kTensor) {
-        float m = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) m = fmaxf(m, fabsf(t.v[i][e]));
-        const uint32_t wm = __float_as_uint(wave_max_nonneg(live ? m : 0.0f));
-        if (lane == 0) wg_max[wave] = wm;
+        const uint32_t wm = __float_as_uint(wave_max_nonneg(tmax));
+        if (lane == 0) wmax[0][wave][0] = wm;
         __syncthreads();
-        if (threadIdx.x == 0) atomicMax(mx, max(max(wg_max[0], wg_max[1]), max(wg_max[2], wg_max[3])));
-    } else if constexpr (G == kToken) {
-        // row 2i + l/32: max over the 4 elements, then over the 32 lanes of the half-wave
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            float m = 0.0f;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) m = fmaxf(m, fabsf(t.v[i][e]));
-            uint32_t u = live ? __float_as_uint(m) : 0u;
-            u = max(u, dpp<kDppXor1>(u));
-            u = max(u, dpp<kDppXor2>(u));
-            u = max(u, dpp<kDppHalfMirror>(u));
-            u = max(u, dpp<kDppMirror>(u));
-            u = max(u, (uint32_t)__shfl_xor((int)u, 16));
-            if (grp_raw < ngroups && (lane & 31) == 0) atomicMax(mx + t.row0 + 2 * i, u);
-        }
-    } else {
-        // columns col0..col0+3: max over the 16 rows, then with lane l^32
-        uint32_t u[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            float m = 0.0f;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(t.v[i][e]));
-            u[e] = live ? __float_as_uint(m) : 0u;
-            u[e] = max(u[e], (uint32_t)__shfl_xor((int)u[e], 32));
-        }
-        if (grp_raw < ngroups && live && lane < 32)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) atomicMax(mx + t.col0 + e, u[e]);
+        if (threadIdx.x == 0)
+            atomicMax(mx, max(max(wmax[0][0][0], wmax[0][1][0]), max(wmax[0][2][0], wmax[0][3][0])));
     }
 }
 
@@ -150,20 +182,14 @@ __device__ __forceinline__ void add_sq_err(const float (&x)[N], float s, double 
     }
 }
 
+// Errors of one tile's 32 values of a lane under the given scales.
 template <int G>
-__global__ __launch_bounds__(256) void k_qe_err(const float *__restrict__ x, int64_t ldx, int nbc, int ngc,
-                                                int64_t ngroups, const float *__restrict__ s,
-                                                double *__restrict__ sse) {
-    __shared__ double wg_sum[4];
-    const int lane = threadIdx.x & (kWave - 1), wave = wave_id_uniform();
-    const int64_t grp_raw = (int64_t)blockIdx.x * 4 + wave;
-    const Tile t = load_tile(x, ldx, nbc, ngc, min(grp_raw, ngroups - 1));
-    const bool live = grp_raw < ngroups && t.valid;
+__device__ __forceinline__ double tile_err(const Tile &t, const float *__restrict__ s) {
     double acc = 0.0;
     if constexpr (G == kTensor) {
-        const float sc = live ? s[0] : 0.0f;
+        const float sc = s[0];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
+        for (int c = 0; c < kRows / 4; ++c) {
             float v[16];
 #pragma unroll
             for (int k = 0; k < 16; ++k) v[k] = t.v[4 * c + k / 4][k % 4];
@@ -171,88 +197,115 @@ __global__ __launch_bounds__(256) void k_qe_err(const float *__restrict__ x, int
         }
     } else if constexpr (G == kToken) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const float sc = live ? s[t.row0 + 2 * i] : 0.0f;
-            add_sq_err<4>(t.v[i], sc, acc);
-        }
+        for (int i = 0; i < kRows; ++i) add_sq_err<4>(t.v[i], s[t.row0 + i], acc);
     } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const float sc = live ? s[t.col0 + e] : 0.0f;
-            float v[16];
+            float v[kRows];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) v[i] = t.v[i][e];
-            add_sq_err<16>(v, sc, acc);
+            for (int i = 0; i < kRows; ++i) v[i] = t.v[i][e];
+            add_sq_err<kRows>(v, s[t.col0 + e], acc);
         }
     }
-    if (!live) acc = 0.0;
-    // wave sum, then one atomic add per workgroup
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
-    if (lane == 0) wg_sum[wave] = acc;
-    __syncthreads();
-    if (threadIdx.x == 0) atomicAdd(sse, (wg_sum[0] + wg_sum[1]) + (wg_sum[2] + wg_sum[3]));
+    return t.valid ? acc : 0.0;
 }
 
-// 32x32 blocks in one pass: the wavefront holds its four blocks whole, so
-// the block maxima, scales and errors come from registers.
-__global__ __launch_bounds__(256) void k_qe_block(const float *__restrict__ x, int64_t ldx, int nbc, int ngc,
-                                                  int64_t ngroups, float *__restrict__ s,
-                                                  double *__restrict__ sse) {
-    __shared__ double wg_sum[4];
-    const int lane = threadIdx.x & (kWave - 1), wave = wave_id_uniform();
-    const int64_t grp_raw = (int64_t)blockIdx.x * 4 + wave;
-    const Tile t = load_tile(x, ldx, nbc, ngc, min(grp_raw, ngroups - 1));
-    const bool live = grp_raw < ngroups && t.valid;
-    float m = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) m = fmaxf(m, fabsf(t.v[i][e]));
-    uint32_t u = __float_as_uint(m);
-    u = max(u, dpp<kDppXor1>(u));
-    u = max(u, dpp<kDppXor2>(u));
-    u = max(u, dpp<kDppHalfMirror>(u));                  // the 8 lanes of one block row pair
-    u = max(u, (uint32_t)__shfl_xor((int)u, 32));        // and the other half-wave's rows
-    const float sc = block_scale(__uint_as_float(u));
-    if (live && (lane & 39) == 0) s[t.gi * nbc + t.col0 / kBlock] = sc;   // lanes 0, 8, 16, 24
+template <int G>
+__global__ __launch_bounds__(64 * kWaves) void k_qe_err(const float *__restrict__ x, int64_t ldx, int nbc, int nseg,
+                                                        int spw, int sg0, int band0, const float *__restrict__ s,
+                                                        double *__restrict__ sse) {
+    const int band = band0 + blockIdx.y, seg_first = (sg0 + blockIdx.x) * spw;
     double acc = 0.0;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        float v[16];
-#pragma unroll
-        for (int k = 0; k < 16; ++k) v[k] = t.v[4 * c + k / 4][k % 4];
-        add_sq_err<16>(v, sc, acc);
+    Tile t = load_tile(x, ldx, nbc, min(seg_first, nseg - 1), band);
+#pragma unroll 1
+    for (int j = 0; j < spw && seg_first + j < nseg; ++j) {
+        const Tile nt = load_tile(x, ldx, nbc, min(seg_first + j + 1, nseg - 1), band);   // prefetch
+        acc += tile_err<G>(t, s);
+        t = nt;
     }
-    if (!live) acc = 0.0;
+    wg_sum_add(acc, sse);
+}
+
+// 32x32 blocks in one pass: block maxima inside the wavefront by DPP (a
+// block's 8 lanes are adjacent), then across the four wavefronts through LDS
+// (two buffers: one barrier per segment); scales and errors from registers.
+__global__ __launch_bounds__(64 * kWaves) void k_qe_block(const float *__restrict__ x, int64_t ldx, int nbc,
+                                                          int nseg, int spw, int sg0, int band0, float *__restrict__ s,
+                                                          double *__restrict__ sse) {
+    __shared__ __attribute__((aligned(16))) float red[2][kSegBlocks][kWaves];
+    const int lane = threadIdx.x & (kWave - 1), wave = wave_id_uniform();
+    const int band = band0 + blockIdx.y, seg_first = (sg0 + blockIdx.x) * spw;
+    const int b = lane / 8;
+    double acc = 0.0;
+    Tile t = load_tile(x, ldx, nbc, min(seg_first, nseg - 1), band);
+#pragma unroll 1
+    for (int j = 0; j < spw && seg_first + j < nseg; ++j) {
+        const Tile nt = load_tile(x, ldx, nbc, min(seg_first + j + 1, nseg - 1), band);   // prefetch
+        float m = 0.0f;
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
-    if (lane == 0) wg_sum[wave] = acc;
-    __syncthreads();
-    if (threadIdx.x == 0) atomicAdd(sse, (wg_sum[0] + wg_sum[1]) + (wg_sum[2] + wg_sum[3]));
+        for (int i = 0; i < kRows; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) m = fmaxf(m, fabsf(t.v[i][e]));
+        uint32_t u = __float_as_uint(m);
+        u = max(u, dpp<kDppXor1>(u));
+        u = max(u, dpp<kDppXor2>(u));
+        u = max(u, dpp<kDppHalfMirror>(u));              // the 8 lanes of one block
+        if ((lane & 7) == 0) red[j & 1][b][wave] = __uint_as_float(u);
+        __syncthreads();
+        const f32x4 r = *reinterpret_cast<const f32x4 *>(red[j & 1][b]);
+        const float sc = block_scale(fmaxf(fmaxf(r.x, r.y), fmaxf(r.z, r.w)));
+        if (t.valid && wave == 0 && (lane & 7) == 0) s[(int64_t)band * nbc + t.bj] = sc;
+        double a = 0.0;
+#pragma unroll
+        for (int c = 0; c < kRows / 4; ++c) {
+            float v[16];
+#pragma unroll
+            for (int k = 0; k < 16; ++k) v[k] = t.v[4 * c + k / 4][k % 4];
+            add_sq_err<16>(v, sc, a);
+        }
+        acc += t.valid ? a : 0.0;
+        t = nt;
+    }
+    wg_sum_add(acc, sse);
+}
+
+template <typename L>
+void for_grid(int64_t nbr, int64_t nsg, L &&launch) {
+    for (int64_t b0 = 0; b0 < nbr; b0 += kMaxGridY)
+        for (int64_t s0 = 0; s0 < nsg; s0 += kMaxGridX)
+            launch(b0, s0, dim3((unsigned)std::min<int64_t>(kMaxGridX, nsg - s0),
+                                (unsigned)std::min<int64_t>(kMaxGridY, nbr - b0)));
 }
 
 template <int G>
 hipError_t launch_g(const float *x, int64_t ldx, int64_t rows, int64_t cols, float *s, double *sse,
                     hipStream_t stream) {
     const int64_t nbr = rows / kBlock, nbc = cols / kBlock;
-    const int64_t ngc = (nbc + kGroup - 1) / kGroup, ngroups = nbr * ngc;
+    const int64_t nseg = (nbc + kSegBlocks - 1) / kSegBlocks;
+    // segments per workgroup: as many as keep at least 1024 workgroups
+    int spw = kMaxSegPerWG;
+    while (spw > 1 && nbr * ((nseg + spw - 1) / spw) < 1024) spw /= 2;
+    const int64_t nsg = (nseg + spw - 1) / spw;
     const int64_t ng = G == kBlockG ? 0 : G == kToken ? rows : G == kChannel ? cols : 1;   // maxima to clear
     uint32_t *mx = reinterpret_cast<uint32_t *>(s);
     // zero the atomically combined maxima and the sum (block scales are
     // written whole by the one-pass kernel)
     hipLaunchKernelGGL(k_qe_init, dim3((unsigned)((ng + 256) / 256)), dim3(256), 0, stream, mx, ng, sse);
-    if (ngroups == 0) return hipGetLastError();
-    const unsigned grid = (unsigned)((ngroups + 3) / 4);
-    if constexpr (G == kBlockG) {
-        hipLaunchKernelGGL(k_qe_block, dim3(grid), dim3(256), 0, stream, x, ldx, (int)nbc, (int)ngc, ngroups, s,
-                           sse);
-    } else {
-        hipLaunchKernelGGL(k_qe_max<G>, dim3(grid), dim3(256), 0, stream, x, ldx, (int)nbc, (int)ngc, ngroups,
-                           mx);
+    if (nbr == 0 || nbc == 0) return hipGetLastError();
+    for_grid(nbr, nsg, [&](int64_t b0, int64_t s0, dim3 grid) {
+        if constexpr (G == kBlockG)
+            hipLaunchKernelGGL(k_qe_block, grid, dim3(64 * kWaves), 0, stream, x, ldx, (int)nbc, (int)nseg, spw,
+                               (int)s0, (int)b0, s, sse);
+        else
+            hipLaunchKernelGGL(k_qe_max<G>, grid, dim3(64 * kWaves), 0, stream, x, ldx, (int)nbc, (int)nseg, spw,
+                               (int)s0, (int)b0, mx);
+    });
+    if constexpr (G != kBlockG) {
         hipLaunchKernelGGL(k_qe_scale, dim3((unsigned)((ng + 255) / 256)), dim3(256), 0, stream, mx, ng);
-        hipLaunchKernelGGL(k_qe_err<G>, dim3(grid), dim3(256), 0, stream, x, ldx, (int)nbc, (int)ngc, ngroups,
-                           (const float *)s, sse);
+        for_grid(nbr, nsg, [&](int64_t b0, int64_t s0, dim3 grid) {
+            hipLaunchKernelGGL(k_qe_err<G>, grid, dim3(64 * kWaves), 0, stream, x, ldx, (int)nbc, (int)nseg, spw,
+                               (int)s0, (int)b0, (const float *)s, sse);
+        });
     }
     return hipGetLastError();
 }

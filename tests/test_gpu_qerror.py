@@ -46,6 +46,16 @@ def test_shapes(gran, rows, cols):
 
 
 @pytest.mark.parametrize("gran", GRANS)
+def test_segments_in_turn_ragged(gran):
+    """8192 x 2080: 65 block columns in 9 row segments, so each workgroup takes
+    two segments in turn and the last takes one, itself ragged (one block)."""
+    rows, cols = 8192, 2080
+    x = inputs.activation(420, 0, rows, cols, n_outlier_cols=21, factor=60.0)
+    sse = check(dev(x), x, gran, f"{rows}x{cols}")
+    note(f"quant_error {gran} {rows}x{cols}: mse {sse / x.size:.4e}")
+
+
+@pytest.mark.parametrize("gran", GRANS)
 def test_strided_view(gran):
     rows, cols = 96, 224
     x = inputs.activation(410, 0, rows, cols, n_outlier_cols=3, factor=80.0)
