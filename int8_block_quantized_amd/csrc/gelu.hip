@@ -13,13 +13,16 @@
 //
 // Per block, every element is x = fl(s*q) for one of at most 256 codes, so g
 // is evaluated once per code value, not once per element:
-//   1. the block's largest code c_max: a max over the block's 16 lanes (two
-//      DPP steps and four readlanes per block);
+//   1. the block's largest code c_max: packed 16-bit maxima over the lane's
+//      bytes, then a max over the block's 16 lanes (two DPP steps within
+//      each row of 16 lanes, two row-swapping permutes across the rows), so
+//      every lane holds its own block's;
 //   2. for x >= 0, g is increasing, and for x < 0, |g| < 0.16998; so when
 //      c_max > 0 and g(c_max) >= 0.17 the block max |g| is g(c_max),
-//      evaluated in binary64 (lanes 0..3 do the four blocks of a group at
-//      once).  Otherwise (blocks with almost no positive mass) every
-//      element's |g| is looked up in a table evaluated in binary64;
+//      evaluated in binary64 (one call for the eight blocks of both passes,
+//      with their output scales).  Otherwise (blocks with almost no positive
+//      mass) every element's |g| is looked up in a table evaluated in
+//      binary64;
 //   3. s' = fl(max/127); lane l evaluates g for the codes +-(2l+1) and
 //      +-(2l+2) in binary32 (gelu_fast's polynomial tail approximation: one
 //      tail value per pair, as g(x) = x - xQ(x) and g(-x) = -xQ(x)) and turns
@@ -27,8 +30,11 @@
 //      reference, see there), bytes of the block's 256-entry code table in
 //      LDS, indexed by the code's raw byte;
 //   4. each element's output code is one byte read from its block's table (a
-//      256-byte table spans the 64 LDS banks once, so the reads never
-//      conflict).
+//      256-byte table spans the 64 LDS banks once, so reads of one table
+//      never conflict; the four tables of a group share the banks, so one
+//      instruction's reads can).
+// The kernel is VALU-bound (the table work and the lookups' address and
+// packing permutes), not HBM-bound.
 // HBM traffic is the algorithmic 2 bytes per element plus 8 bytes per block.
 #include "jf_device.h"
 #include "jf_gelu.h"
@@ -43,34 +49,46 @@ __device__ __attribute__((noinline)) float gelu_ref_outlined(float x) { return g
 
 // Output codes of a lane's table entries.  g holds gelu_fast values, s2 =
 // fl(m/127) with m = gelu_ref of the block's largest code, m >= 0.17, so the
-// table inputs satisfy |x| >= 0.0022 or x = 0.  In units of s2 the gap
-// between g and gref is at most 127 * 6.51e-7 = 8.3e-5 for x >= 0 and
-// 2.14e-7 * 127 / 0.17 = 1.6e-4 for x < 0; with r = rcp(s2) (hardware
-// reciprocal, within 1 ulp: at most 1.6e-5 on a quotient below 128) and the
-// roundings of t = fl(g*r) and of the reference quotient fl(gref/s2) (each
-// <= 2^-18), t is within 1.9e-4 of fl(gref/s2).  So rne(t) is the reference
-// code unless t is within 2^-12 of a half-integer; those entries (about
-// 4.9e-4 of them) are recomputed from gelu_ref with an IEEE division.
+// table inputs satisfy |x| >= 0.0022 or x = 0, where gelu_fast is within
+// 6.51e-7 |gref| of gref = gelu_ref(x) for x >= 0 and within 2.14e-7 of it
+// for x < 0.  Let r = rcp(s2) (hardware reciprocal, within one ulp, i.e.
+// 2^-23 relative), t = fl(g r) and Q = fl(gref / s2), the quotient whose
+// rne is the reference code.  Collecting the reciprocal's error and the two
+// products' roundings (2^-24 each) with the error of g:
+//   x >= 0: |t - Q| <= (6.51e-7 + 2.4e-7) |t|  <  1e-6 |t|,
+//   x <  0: |t - Q| <= 2.15e-7 r + 2.4e-7 |t|  <  2.2e-7 r + 1e-6 |t|.
+// So with w = 1e-6 |t| + 2.2e-7 r, rne(t) = rne(Q) whenever t is more than
+// w away from the nearest half-integer (t - rne(t) is exact); the test uses
+// w + 2^-20, which covers its own roundings.  The other entries (about
+// 1.5e-4 of the positive ones at the bench input's scales, far fewer of the
+// negative ones) are recomputed from gelu_ref with an IEEE division, one
+// wavefront-wide binary64 call per round.
 template <int N>
 __device__ __forceinline__ void table_codes(const float (&g)[N], const float (&x)[N], float s2, int (&code)[N]) {
     const float r = __builtin_amdgcn_rcpf(s2);
+    const float half_c = 0.5f - __builtin_fmaf(2.2e-7f, r, 0x1p-20f);
     float n[N];
-    bool near = false;
+    uint32_t near = 0;
 #pragma unroll
     for (int j = 0; j < N; ++j) {
         const float t = g[j] * r;
         n[j] = __builtin_rintf(t);
-        near |= fabsf(t - n[j]) > 0.5f - 0x1p-12f;   // |t - rne(t)| <= 1/2 always
+        if (fabsf(t - n[j]) > __builtin_fmaf(-1e-6f, fabsf(t), half_c)) near |= 1u << j;
     }
-    if (__builtin_amdgcn_ballot_w64(near) != 0) {
+    while (__builtin_amdgcn_ballot_w64(near != 0) != 0) {
+        if (near != 0) {
+            const int k = __builtin_ctz(near);
+            near &= near - 1;
+            float xk = x[0];
 #pragma unroll
-        for (int j = 0; j < N; ++j) {
-            const float t = g[j] * r;
-            if (fabsf(t - n[j]) > 0.5f - 0x1p-12f) n[j] = __builtin_rintf(gelu_ref_outlined(x[j]) / s2);
+            for (int j = 1; j < N; ++j) xk = k == j ? x[j] : xk;
+            const float nk = __builtin_rintf(gelu_ref_outlined(xk) / s2);
+#pragma unroll
+            for (int j = 0; j < N; ++j) n[j] = k == j ? nk : n[j];
         }
     }
 #pragma unroll
-    for (int j = 0; j < N; ++j) code[j] = (int)fminf(fmaxf(n[j], -127.0f), 127.0f);
+    for (int j = 0; j < N; ++j) code[j] = (int)__builtin_amdgcn_fmed3f(n[j], -127.0f, 127.0f);   // n is finite
 }
 
 constexpr int kGroup = 4;    // horizontally adjacent blocks per wavefront pass
@@ -80,34 +98,44 @@ typedef short s16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) const uint8_t lds_u8;
 
-// Largest signed code among the 16 bytes of a lane (packed 16-bit maxima).
-__device__ __forceinline__ int max_code(const uint32_t (&wd)[4]) {
-    s16x2 m = {-128, -128};
+// Largest signed code among a lane's 64 bytes of one pass.  Read as two
+// signed 16-bit halves, a dword orders each half by its high byte (bytes 1
+// and 3); shifted left by 8 within each half, by its low byte (bytes 0 and
+// 2).  Three packed instructions per dword, one reduction at the end.
+__device__ __forceinline__ int max_code(const u32x4 (&w)[4]) {
+    s16x2 hi = __builtin_bit_cast(s16x2, w[0].x), lo = hi << 8;
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
-        const s16x2 v = __builtin_bit_cast(s16x2, wd[d]);
-        const s16x2 even = (s16x2)(v << 8) >> 8;   // bytes 0 and 2, sign-extended
-        const s16x2 odd = v >> 8;                  // bytes 1 and 3, sign-extended
-        m = __builtin_elementwise_max(m, __builtin_elementwise_max(even, odd));
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t wd[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
+#pragma unroll
+        for (int d = (i == 0 ? 1 : 0); d < 4; ++d) {
+            const s16x2 v = __builtin_bit_cast(s16x2, wd[d]);
+            hi = __builtin_elementwise_max(hi, v);
+            lo = __builtin_elementwise_max(lo, (s16x2)(v << 8));
+        }
     }
+    const s16x2 m = __builtin_elementwise_max(hi, lo) >> 8;
     return max((int)m.x, (int)m.y);
 }
 
 // Maximum over the 16 lanes holding one block (lanes 8r + 2b + e): DPP over
-// lane bits 0 and 3, then one readlane per row of 16.  Returns block b's
-// value (wave-uniform).
+// lane bits 0 and 3 within each row of 16 lanes, ...
 __device__ __forceinline__ uint32_t group_reduce_rows(uint32_t v) {
     v = max(v, dpp<kDppXor1>(v));
     return max(v, dpp<kDppRowRor8>(v));
 }
+// ... then across the four rows (lane bits 5 and 4) with the row-swapping
+// permutes: afterwards every lane holds the maximum of its own block.
+__device__ __forceinline__ uint32_t wave_rows_max(uint32_t v) {
+    const auto h = __builtin_amdgcn_permlane32_swap(v, v, false, false);   // lanes l and l ^ 32
+    v = max(h[0], h[1]);
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);   // lanes l and l ^ 16
+    return max(r[0], r[1]);
+}
+// Block b's maximum for the slow path (wave-uniform), from the row maxima.
 __device__ __forceinline__ uint32_t block_max_u(uint32_t v_rows, int b) {
     const uint32_t a = __builtin_amdgcn_readlane(v_rows, 2 * b), c = __builtin_amdgcn_readlane(v_rows, 16 + 2 * b);
     const uint32_t d = __builtin_amdgcn_readlane(v_rows, 32 + 2 * b), e = __builtin_amdgcn_readlane(v_rows, 48 + 2 * b);
-    return max(max(a, c), max(d, e));
-}
-__device__ __forceinline__ int block_max_i(int v_rows, int b) {
-    const int a = __builtin_amdgcn_readlane(v_rows, 2 * b), c = __builtin_amdgcn_readlane(v_rows, 16 + 2 * b);
-    const int d = __builtin_amdgcn_readlane(v_rows, 32 + 2 * b), e = __builtin_amdgcn_readlane(v_rows, 48 + 2 * b);
     return max(max(a, c), max(d, e));
 }
 
@@ -137,28 +165,19 @@ __global__ __launch_bounds__(256) void k_gelu_i8(const int8_t *__restrict__ q, i
         scl[p] = s[gi * nbc + bj];
     }
 
-    // Largest code of every block of both passes, and g of each block's
-    // largest code in binary64: one call, lane kGroup*p + bb evaluating
-    // block bb of pass p.
-    int cm_rows[kPasses];
-    float xt = 0.0f;
+    // Largest code of every block of both passes (each lane: its own
+    // block's), and g of it in binary64 for all eight blocks in one call:
+    // lanes 16p + 2bb hold block bb of pass p.
+    static_assert(kPasses == 2, "one binary64 call serves two passes");
+    int cm_all[kPasses];
 #pragma unroll
-    for (int p = 0; p < kPasses; ++p) {
-        int cm = -128;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t wd[4] = {w[p][i].x, w[p][i].y, w[p][i].z, w[p][i].w};
-            cm = max(cm, max_code(wd));
-        }
-        // per row of 16 lanes; block_max_i finishes it per block
-        cm_rows[p] = (int)group_reduce_rows((uint32_t)(cm + 128)) - 128;
-#pragma unroll
-        for (int bb = 0; bb < kGroup; ++bb) {
-            const float scb = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(scl[p]), 2 * bb));
-            if (lane == kGroup * p + bb) xt = scb * (float)block_max_i(cm_rows[p], bb);
-        }
-    }
+    for (int p = 0; p < kPasses; ++p)
+        cm_all[p] = (int)wave_rows_max(group_reduce_rows((uint32_t)(max_code(w[p]) + 128))) - 128;
+    const bool second = (lane & 16) != 0;
+    const float xt = (second ? scl[1] : scl[0]) * (float)(second ? cm_all[1] : cm_all[0]);
     const float gt_lane = gelu_ref_outlined(xt);
+    const float s2_lane = block_scale(gt_lane);   // the output scales of the fast path
+    const float kf[2] = {(float)(2 * lane + 1), (float)(2 * lane + 2)};   // the lane's table magnitudes
 
 #pragma unroll
     for (int p = 0; p < kPasses; ++p) {
@@ -171,9 +190,9 @@ __global__ __launch_bounds__(256) void k_gelu_i8(const int8_t *__restrict__ q, i
 #pragma unroll
         for (int bb = 0; bb < kGroup; ++bb) {
             if (bb >= nb) break;
-            const int cmax = block_max_i(cm_rows[p], bb);
+            const int cmax = __builtin_amdgcn_readlane(cm_all[p], 2 * bb);
             const float sc = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(scl[p]), 2 * bb));
-            const float gtop = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(gt_lane), kGroup * p + bb));
+            const float gtop = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(gt_lane), 16 * p + 2 * bb));
             float x[4], g[4];
             int code[4] = {0, 0, 0, 0};
             float s2;
@@ -184,14 +203,14 @@ __global__ __launch_bounds__(256) void k_gelu_i8(const int8_t *__restrict__ q, i
                 // pair p = 128 only has its negative code.
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
-                    const float xp = sc * (float)(2 * lane + h + 1);
+                    const float xp = sc * kf[h];
                     const float q = gelu_tail_q(xp);
                     x[2 * h] = xp;
                     g[2 * h] = xp - xp * q;
                     x[2 * h + 1] = -xp;
                     g[2 * h + 1] = -xp * q;
                 }
-                s2 = block_scale(gtop);
+                s2 = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(s2_lane), 16 * p + 2 * bb));
                 table_codes(g, x, s2, code);
                 uint8_t *tb = reinterpret_cast<uint8_t *>(tables[wave][bb]);
 #pragma unroll
