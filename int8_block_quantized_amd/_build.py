@@ -27,22 +27,27 @@ def sources():
     return sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")))
 
 
-TEST_PROBE_SRC = os.path.join(ROOT, "tests", "gelu_bound_check.hip")
-TEST_PROBE_BIN = os.path.join(ROOT, "tests", "gelu_bound_check")
+# exhaustive checks of the GELU kernels' elementary-function evaluations,
+# run by the GPU tests
+TEST_PROBES = ("gelu_bound_check", "gelu_grad_check")
 
 
-def build_test_probe(verbose: bool = False) -> str:
-    """Compile the exhaustive GELU error check used by the GPU tests."""
-    tmp = TEST_PROBE_BIN + ".tmp"
-    cmd = ["hipcc", "--offload-arch=gfx950", "-O3", "-ffp-contract=off",
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", TEST_PROBE_SRC, "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed:\n{res.stdout}\n{res.stderr}")
-    os.replace(tmp, TEST_PROBE_BIN)
-    return TEST_PROBE_BIN
+def build_test_probe(verbose: bool = False) -> list:
+    """Compile the exhaustive GELU / GELU' checks used by the GPU tests."""
+    built = []
+    for name in TEST_PROBES:
+        src, out = os.path.join(ROOT, "tests", name + ".hip"), os.path.join(ROOT, "tests", name)
+        tmp = out + ".tmp"
+        cmd = ["hipcc", "--offload-arch=gfx950", "-O3", "-ffp-contract=off",
+               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", src, "-o", tmp]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError(f"hipcc failed:\n{res.stdout}\n{res.stderr}")
+        os.replace(tmp, out)
+        built.append(out)
+    return built
 
 
 def build(verbose: bool = False) -> str:

@@ -1,0 +1,58 @@
+// jf_gelu_grad.h -- GELU'(z) and GELU'(-z) in binary64 for the INT8 GELU
+// backward's derivative tables.  Written by gen_gelu_grad.py (Chebyshev
+// interpolant of the scaled normal tail M(z) = Q(z) exp(z^2/2) in
+// t = (z - 4)/(z + 4), degree 24; largest relative error of M's binary64
+// evaluation on [0, 40]: 4.50e-16).  Do not edit by hand.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace jf {
+
+constexpr double kGradK = 4.0;
+constexpr int kGradDegree = 24;
+__device__ constexpr double kGradPoly[kGradDegree + 1] = {
+    0x1.82b4bb8c94dcep-3,  // t^0
+    -0x1.373e3a893c28cp-3,  // t^1
+    0x1.8c6dbf2cfc2afp-4,  // t^2
+    -0x1.7dff2bff68052p-5,  // t^3
+    0x1.eec4cc3e4db3ep-7,  // t^4
+    -0x1.ee2761054e5e1p-10,  // t^5
+    -0x1.c81719d60dcdbp-11,  // t^6
+    0x1.ab825ff09481bp-12,  // t^7
+    0x1.17a4aec9fa29ap-15,  // t^8
+    -0x1.e4a431b3465b0p-15,  // t^9
+    -0x1.001f7d33a2ff5p-21,  // t^10
+    0x1.26d193750d626p-17,  // t^11
+    0x1.80ca2044c09bdp-23,  // t^12
+    -0x1.8d64fadf80ed1p-20,  // t^13
+    -0x1.523a2fde9b829p-23,  // t^14
+    0x1.1319f41c90a11p-22,  // t^15
+    0x1.24d40b9cf1122p-24,  // t^16
+    -0x1.5739b1a22c213p-25,  // t^17
+    -0x1.763bb001aa685p-26,  // t^18
+    0x1.33354e7ae3599p-28,  // t^19
+    0x1.7329462b6b607p-28,  // t^20
+    -0x1.4b02181dd18fdp-33,  // t^21
+    -0x1.04ffdbe7bdef2p-30,  // t^22
+    -0x1.0236305d3fd38p-35,  // t^23
+    0x1.828df1c3afaadp-34,  // t^24
+};
+
+// GELU'(z) (.x) and GELU'(-z) (.y) for z >= 0, each rounded once to
+// binary32: d = exp(-z^2/2) (M(z) - z/sqrt(2 pi)) = Q(z) - z phi(z) is
+// GELU'(-z) and 1 - d is GELU'(z).  z*z is exact in binary64 (z is a
+// binary32 value).
+__device__ __forceinline__ float2 gelu_grad_pair_fast(float z) {
+    const double zd = (double)z;
+    const double w = 1.0 / (zd + kGradK);
+    const double t = (zd - kGradK) * w;
+    double p = kGradPoly[kGradDegree];
+#pragma unroll
+    for (int k = kGradDegree - 1; k >= 0; --k) p = __builtin_fma(p, t, kGradPoly[k]);
+    const double m = p * (kGradK * w);
+    const double d = exp(-0.5 * (zd * zd)) * (m - zd * 0.39894228040143267794);
+    return make_float2((float)(1.0 - d), (float)d);
+}
+
+}  // namespace jf

@@ -1,0 +1,84 @@
+"""CPU check of the coefficients in jf_gelu_grad.h (the binary64 expansion the
+INT8 GELU backward kernel uses for its derivative tables).
+
+M(z) = Q(z) exp(z^2/2), Q the upper normal tail, is evaluated from the
+header's power-basis coefficients in t = (z - K)/(z + K) exactly as the
+kernel does (binary64 Horner), and compared with 50-digit mpmath: relative
+error below 1e-15 on [0, 40].  The GELU' pair built from it must round to the
+correctly rounded binary32 values of Phi(x) + x phi(x) (50-digit mpmath) on a
+seeded sample of inputs and at the special points x = 0, the zero of GELU'
+near -0.7518 and the tails.
+"""
+import os
+import re
+
+import mpmath as mp
+import numpy as np
+
+HDR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                   "int8_block_quantized_amd", "csrc", "jf_gelu_grad.h")
+
+
+def header_constants():
+    text = open(HDR).read()
+    k = float(re.search(r"kGradK = ([0-9.]+);", text).group(1))
+    n = int(re.search(r"kGradDegree = (\d+);", text).group(1))
+    coeffs = [float.fromhex(c) for c in re.findall(r"^\s+(-?0x[0-9a-fp.+-]+),\s+// t\^\d+$", text, re.M)]
+    assert len(coeffs) == n + 1
+    return k, coeffs
+
+
+def m_header(z, k, a):
+    w = 1.0 / (z + k)
+    t = (z - k) * w
+    p = a[-1]
+    for v in reversed(a[:-1]):
+        p = p * t + v
+    return p * (k * w)
+
+
+def pair_header(x, k, a):
+    z = float(x)
+    d = np.exp(-0.5 * (z * z)) * (m_header(z, k, a) - z * 0.39894228040143267794)
+    return np.float32(1.0 - d), np.float32(d)
+
+
+def grad_exact(x):
+    x = mp.mpf(float(x))
+    return mp.erfc(-x / mp.sqrt(2)) / 2 + x * mp.exp(-x * x / 2) / mp.sqrt(2 * mp.pi)
+
+
+def to_f32(v):
+    # correctly rounded binary32 of a 50-digit value (via an exact rational
+    # comparison with the two binary32 neighbours of its binary64 image)
+    f = np.float32(float(v))
+    lo, hi = np.nextafter(f, np.float32(-np.inf)), np.nextafter(f, np.float32(np.inf))
+    best = min((f, lo, hi), key=lambda c: abs(mp.mpf(float(c)) - v))
+    return best
+
+
+def test_scaled_tail_relative_error():
+    mp.mp.dps = 50
+    k, a = header_constants()
+    zs = list(np.linspace(0, 2, 201)) + list(np.linspace(2, 40, 191)) + [1e-30, 1e-8, 0.75, 0.7518]
+    worst = 0.0
+    for z in zs:
+        z = float(z)
+        zm = mp.mpf(z)
+        ref = mp.erfc(zm / mp.sqrt(2)) / 2 * mp.exp(zm * zm / 2)
+        worst = max(worst, float(abs(mp.mpf(m_header(z, k, a)) - ref) / ref))
+    assert worst < 1e-15, worst
+
+
+def test_pair_rounds_like_the_exact_derivative():
+    mp.mp.dps = 50
+    k, a = header_constants()
+    g = np.random.default_rng(7)
+    xs = np.concatenate([g.uniform(0, 15, 1500), 10 ** g.uniform(-7, 1.1, 500),
+                         [0.0, 0.7518, 0.75183, 5.9, 14.0, 14.5, 20.0]]).astype(np.float32)
+    bad = 0
+    for x in xs:
+        pos, neg = pair_header(x, k, a)
+        bad += int(pos != to_f32(grad_exact(x))) + int(neg != to_f32(grad_exact(-x)))
+    assert bad == 0, bad
+    assert pair_header(np.float32(0), k, a) == (np.float32(0.5), np.float32(0.5))

@@ -89,3 +89,21 @@ def test_mlp_hidden_gradient_full_size():
     oq, os_ = oracle.gelu_bwd(host(qd), host(sd), host(qh), host(sh))
     frac, srel = assert_requant_close(gq, gs, oq, os_, "mlp 8192x4096")
     note(f"gelu_bwd mlp: code diffs {frac:.2e}, scale rel {srel:.1e}")
+
+
+def test_binary64_derivative_expansion_exhaustive():
+    """The derivative tables evaluate GELU'(z) and GELU'(-z) with a binary64
+    polynomial expansion of the scaled normal tail (jf_gelu_grad.h) instead of
+    the device library's erfc and exp.  Over every finite binary32 z >= 0 the
+    two outputs, rounded to binary32, must equal those of the library formula
+    except on at most 1e-7 of them, and there by one ulp (both are binary64
+    evaluations within a few binary64 ulps of the exact value)."""
+    import os
+    import subprocess
+
+    exe = os.path.join(os.path.dirname(os.path.abspath(__file__)), "gelu_grad_check")
+    assert os.path.exists(exe), "tests/gelu_grad_check is not built (run __graft_entry__.build())"
+    out = subprocess.run([exe], capture_output=True, text=True, timeout=120, check=True).stdout.split()
+    ndiff, worst = int(out[0]), int(out[1])
+    note(f"GELU' expansion vs library erfc/exp: {ndiff} of 2^32 outputs differ, by at most {worst} ulp")
+    assert worst <= 1 and ndiff <= 2 ** 32 * 1e-7
