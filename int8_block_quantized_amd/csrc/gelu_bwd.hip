@@ -18,7 +18,7 @@
 // |y| (DPP within rows of 16 lanes, readlanes across them), s = fl(max/127)
 // and the exact codes of quant_codes.
 // HBM traffic: 2 bytes in + 1 byte out per element, 12 bytes per block.
-#include "jf_gelu_grad.h"
+#include "jf_gelu.h"
 #include "jf_group.h"
 #include "jf_launch.h"
 
@@ -31,9 +31,9 @@ typedef __attribute__((address_space(3))) const float lds_f32;
 constexpr int kGroup = kGroupBlocks;   // horizontally adjacent blocks per wavefront
 
 // GELU' at x and -x (x >= 0) in binary64, each rounded once: the scaled
-// normal-tail expansion of jf_gelu_grad.h (one exp and one division; a
-// library erfc and exp cost about three times as many instructions).
-__device__ __forceinline__ float2 gelu_grad_pair(float x) { return gelu_grad_pair_fast(x); }
+// normal-tail expansion (one exp and one division; a library erfc and exp
+// cost about three times as many instructions).
+__device__ __forceinline__ float2 gelu_grad_pair(float x) { return gelu_grad_pair_tail(x); }
 
 __global__ __launch_bounds__(256) void k_gelu_bwd_i8(const int8_t *__restrict__ qdy, int64_t lddy,
                                                      const float *__restrict__ sdy,

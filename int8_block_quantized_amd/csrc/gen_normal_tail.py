@@ -1,11 +1,8 @@
-"""Writes jf_gelu_grad.h: the binary64 evaluation of GELU' used by the INT8
-GELU backward kernel's derivative tables.
+"""Writes jf_normal_tail.h: the binary64 upper normal tail
+Q(z) = erfc(z/sqrt 2)/2 used by the INT8 GELU backward kernel's derivative
+tables (GELU'(x) = Phi(x) + x phi(x), the derivative of the erf form x Phi(x)
+of the Jetfire summary's INT8 data flow, "Approach"; Phi(-z) = Q(z)).
 
-GELU'(x) = Phi(x) + x phi(x) (the derivative of the erf form x Phi(x), the
-non-linear operator of the Jetfire summary's INT8 data flow, "Approach").
-For z >= 0 both GELU'(z) and GELU'(-z) follow from the upper normal tail
-Q(z) = erfc(z/sqrt 2)/2 and phi(z):
-    GELU'(-z) = Q(z) - z phi(z),    GELU'(z) = 1 - GELU'(-z).
 Q is written as Q(z) = M(z) exp(-z^2/2) with M(z) = Q(z) exp(z^2/2), a
 smooth function that decays like 1/(z sqrt(2 pi)).  M is approximated by a
 polynomial in t = (z - K)/(z + K), which maps [0, inf) onto [-1, 1) (the
@@ -16,7 +13,7 @@ with P the degree-N Chebyshev interpolant of M(z) (z + K)/K at the N + 1
 Chebyshev points of t, computed here in 50-digit arithmetic (mpmath) and
 converted to the power basis for Horner's rule.
 
-Run:  python3 gen_gelu_grad.py > jf_gelu_grad.h   (needs mpmath; build-time
+Run:  python3 gen_normal_tail.py > jf_normal_tail.h   (needs mpmath; build-time
 only, nothing at run time imports it).
 """
 import sys
@@ -83,33 +80,27 @@ def main():
     a = power_coefficients()
     err = max_rel_error(a)
     out = sys.stdout
-    out.write("// jf_gelu_grad.h -- GELU'(z) and GELU'(-z) in binary64 for the INT8 GELU\n")
-    out.write("// backward's derivative tables.  Written by gen_gelu_grad.py (Chebyshev\n")
-    out.write("// interpolant of the scaled normal tail M(z) = Q(z) exp(z^2/2) in\n")
+    out.write("// jf_normal_tail.h -- the upper normal tail Q(z) = erfc(z/sqrt 2)/2 in\n")
+    out.write("// binary64 for the INT8 GELU backward.  Written by gen_normal_tail.py\n")
+    out.write("// (Chebyshev interpolant of the scaled tail M(z) = Q(z) exp(z^2/2) in\n")
     out.write(f"// t = (z - {K})/(z + {K}), degree {N}; largest relative error of M's binary64\n")
     out.write(f"// evaluation on [0, 40]: {err:.2e}).  Do not edit by hand.\n")
     out.write("#pragma once\n\n#include <hip/hip_runtime.h>\n\nnamespace jf {\n\n")
-    out.write(f"constexpr double kGradK = {K}.0;\n")
-    out.write(f"constexpr int kGradDegree = {N};\n")
-    out.write("__device__ constexpr double kGradPoly[kGradDegree + 1] = {\n")
+    out.write(f"constexpr double kTailK = {K}.0;\n")
+    out.write(f"constexpr int kTailDegree = {N};\n")
+    out.write("__device__ constexpr double kTailPoly[kTailDegree + 1] = {\n")
     for i, v in enumerate(a):
         out.write(f"    {float.hex(v)},  // t^{i}\n")
     out.write("};\n\n")
     out.write(
-        "// GELU'(z) (.x) and GELU'(-z) (.y) for z >= 0, each rounded once to\n"
-        "// binary32: d = exp(-z^2/2) (M(z) - z/sqrt(2 pi)) = Q(z) - z phi(z) is\n"
-        "// GELU'(-z) and 1 - d is GELU'(z).  z*z is exact in binary64 (z is a\n"
-        "// binary32 value).\n"
-        "__device__ __forceinline__ float2 gelu_grad_pair_fast(float z) {\n"
-        "    const double zd = (double)z;\n"
-        "    const double w = 1.0 / (zd + kGradK);\n"
-        "    const double t = (zd - kGradK) * w;\n"
-        "    double p = kGradPoly[kGradDegree];\n"
+        "// M(z) = Q(z) exp(z^2/2) for z >= 0 (finite): one division, Horner in t.\n"
+        "__device__ __forceinline__ double normal_tail_scaled(double z) {\n"
+        "    const double w = 1.0 / (z + kTailK);\n"
+        "    const double t = (z - kTailK) * w;\n"
+        "    double p = kTailPoly[kTailDegree];\n"
         "#pragma unroll\n"
-        "    for (int k = kGradDegree - 1; k >= 0; --k) p = __builtin_fma(p, t, kGradPoly[k]);\n"
-        "    const double m = p * (kGradK * w);\n"
-        "    const double d = exp(-0.5 * (zd * zd)) * (m - zd * 0.39894228040143267794);\n"
-        "    return make_float2((float)(1.0 - d), (float)d);\n"
+        "    for (int k = kTailDegree - 1; k >= 0; --k) p = __builtin_fma(p, t, kTailPoly[k]);\n"
+        "    return p * (kTailK * w);\n"
         "}\n\n}  // namespace jf\n")
 
 

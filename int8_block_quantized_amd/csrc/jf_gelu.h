@@ -1,4 +1,4 @@
-// jf_gelu.h -- the two GELU evaluations used by the INT8 GELU kernel.
+// jf_gelu.h -- the GELU and GELU' evaluations used by the INT8 GELU kernels.
 //
 // GELU in its erf form (the non-linear operator of the Jetfire summary's INT8
 // data flow, "Approach"): g(x) = x * Phi(x) with Phi the standard normal CDF,
@@ -10,12 +10,26 @@
 
 #include <hip/hip_runtime.h>
 
+#include "jf_normal_tail.h"
+
 namespace jf {
 
 // Reference value: evaluated in binary64, rounded once to binary32.
 __device__ __forceinline__ float gelu_ref(float x) {
     const double xd = (double)x;
     return (float)(xd * (0.5 * erfc(-xd * 0.70710678118654752440)));
+}
+
+// GELU'(z) (.x) and GELU'(-z) (.y) for z >= 0 in binary64 from the
+// normal-tail expansion of jf_normal_tail.h (one exp, one division and a
+// degree-24 polynomial: about a third of the instructions of the library's
+// erfc and exp), each rounded once: d = Q(z) - z phi(z) =
+// exp(-z^2/2) (M(z) - z/sqrt(2 pi)) is GELU'(-z), and
+// GELU'(z) = Phi(z) + z phi(z) = 1 - d.  z*z is exact in binary64.
+__device__ __forceinline__ float2 gelu_grad_pair_tail(float z) {
+    const double zd = (double)z;
+    const double d = exp(-0.5 * (zd * zd)) * (normal_tail_scaled(zd) - zd * 0.39894228040143267794);
+    return make_float2((float)(1.0 - d), (float)d);
 }
 
 // Fast binary32 GELU for the code tables.  Phi(x) = 1 - Q(x) for x >= 0 and

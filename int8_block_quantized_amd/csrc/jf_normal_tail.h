@@ -1,6 +1,6 @@
-// jf_gelu_grad.h -- GELU'(z) and GELU'(-z) in binary64 for the INT8 GELU
-// backward's derivative tables.  Written by gen_gelu_grad.py (Chebyshev
-// interpolant of the scaled normal tail M(z) = Q(z) exp(z^2/2) in
+// jf_normal_tail.h -- the upper normal tail Q(z) = erfc(z/sqrt 2)/2 in
+// binary64 for the INT8 GELU backward.  Written by gen_normal_tail.py
+// (Chebyshev interpolant of the scaled tail M(z) = Q(z) exp(z^2/2) in
 // t = (z - 4)/(z + 4), degree 24; largest relative error of M's binary64
 // evaluation on [0, 40]: 4.50e-16).  Do not edit by hand.
 #pragma once
@@ -9,9 +9,9 @@
 
 namespace jf {
 
-constexpr double kGradK = 4.0;
-constexpr int kGradDegree = 24;
-__device__ constexpr double kGradPoly[kGradDegree + 1] = {
+constexpr double kTailK = 4.0;
+constexpr int kTailDegree = 24;
+__device__ constexpr double kTailPoly[kTailDegree + 1] = {
     0x1.82b4bb8c94dcep-3,  // t^0
     -0x1.373e3a893c28cp-3,  // t^1
     0x1.8c6dbf2cfc2afp-4,  // t^2
@@ -39,20 +39,14 @@ __device__ constexpr double kGradPoly[kGradDegree + 1] = {
     0x1.828df1c3afaadp-34,  // t^24
 };
 
-// GELU'(z) (.x) and GELU'(-z) (.y) for z >= 0, each rounded once to
-// binary32: d = exp(-z^2/2) (M(z) - z/sqrt(2 pi)) = Q(z) - z phi(z) is
-// GELU'(-z) and 1 - d is GELU'(z).  z*z is exact in binary64 (z is a
-// binary32 value).
-__device__ __forceinline__ float2 gelu_grad_pair_fast(float z) {
-    const double zd = (double)z;
-    const double w = 1.0 / (zd + kGradK);
-    const double t = (zd - kGradK) * w;
-    double p = kGradPoly[kGradDegree];
+// M(z) = Q(z) exp(z^2/2) for z >= 0 (finite): one division, Horner in t.
+__device__ __forceinline__ double normal_tail_scaled(double z) {
+    const double w = 1.0 / (z + kTailK);
+    const double t = (z - kTailK) * w;
+    double p = kTailPoly[kTailDegree];
 #pragma unroll
-    for (int k = kGradDegree - 1; k >= 0; --k) p = __builtin_fma(p, t, kGradPoly[k]);
-    const double m = p * (kGradK * w);
-    const double d = exp(-0.5 * (zd * zd)) * (m - zd * 0.39894228040143267794);
-    return make_float2((float)(1.0 - d), (float)d);
+    for (int k = kTailDegree - 1; k >= 0; --k) p = __builtin_fma(p, t, kTailPoly[k]);
+    return p * (kTailK * w);
 }
 
 }  // namespace jf

@@ -1,6 +1,6 @@
-// Exhaustive check of the binary64 GELU' expansion used by the INT8 GELU
-// backward kernel's derivative tables (jf::gelu_grad_pair_fast, a scaled
-// normal-tail polynomial) against the same quantities written with the
+// Exhaustive check of the binary64 GELU' evaluation used by the INT8 GELU
+// backward kernel's derivative tables (jf::gelu_grad_pair_tail, from the
+// scaled normal-tail polynomial) against the same quantities written with the
 // device library's binary64 erfc and exp: Phi(-z) = erfc(z/sqrt 2)/2,
 // z phi(z) = z exp(-z^2/2)/sqrt(2 pi), GELU'(z) = (1 - Phi(-z)) + z phi(z),
 // GELU'(-z) = Phi(-z) - z phi(z), each rounded once to binary32.  Covers
@@ -11,7 +11,7 @@
 #include <hip/hip_runtime.h>
 #include <stdio.h>
 
-#include "../int8_block_quantized_amd/csrc/jf_gelu_grad.h"
+#include "../int8_block_quantized_amd/csrc/jf_gelu.h"
 
 __device__ float2 grad_pair_libm(float z) {
     const double zd = (double)z;
@@ -36,7 +36,7 @@ __global__ void check(unsigned *res) {
         const unsigned u = base + i;
         if (u > 0x7f7fffffu) break;                       // finite, non-negative
         const float z = __uint_as_float(u);
-        const float2 f = jf::gelu_grad_pair_fast(z), r = grad_pair_libm(z);
+        const float2 f = jf::gelu_grad_pair_tail(z), r = grad_pair_libm(z);
         const unsigned dx = ulp_dist(f.x, r.x), dy = ulp_dist(f.y, r.y);
         diff += (dx != 0) + (dy != 0);
         worst = max(worst, max(dx, dy));

@@ -1,5 +1,5 @@
-"""CPU check of the coefficients in jf_gelu_grad.h (the binary64 expansion the
-INT8 GELU backward kernel uses for its derivative tables).
+"""CPU check of the coefficients in jf_normal_tail.h (the binary64 expansion of
+the upper normal tail that the INT8 GELU backward kernel uses for GELU').
 
 M(z) = Q(z) exp(z^2/2), Q the upper normal tail, is evaluated from the
 header's power-basis coefficients in t = (z - K)/(z + K) exactly as the
@@ -16,13 +16,13 @@ import mpmath as mp
 import numpy as np
 
 HDR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
-                   "int8_block_quantized_amd", "csrc", "jf_gelu_grad.h")
+                   "int8_block_quantized_amd", "csrc", "jf_normal_tail.h")
 
 
 def header_constants():
     text = open(HDR).read()
-    k = float(re.search(r"kGradK = ([0-9.]+);", text).group(1))
-    n = int(re.search(r"kGradDegree = (\d+);", text).group(1))
+    k = float(re.search(r"kTailK = ([0-9.]+);", text).group(1))
+    n = int(re.search(r"kTailDegree = (\d+);", text).group(1))
     coeffs = [float.fromhex(c) for c in re.findall(r"^\s+(-?0x[0-9a-fp.+-]+),\s+// t\^\d+$", text, re.M)]
     assert len(coeffs) == n + 1
     return k, coeffs
@@ -82,3 +82,4 @@ def test_pair_rounds_like_the_exact_derivative():
         bad += int(pos != to_f32(grad_exact(x))) + int(neg != to_f32(grad_exact(-x)))
     assert bad == 0, bad
     assert pair_header(np.float32(0), k, a) == (np.float32(0.5), np.float32(0.5))
+
