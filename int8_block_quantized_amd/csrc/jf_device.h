@@ -63,9 +63,7 @@ __device__ __forceinline__ float block_scale(float absmax) { return absmax / 127
 // Code of one value under a non-zero scale: correctly rounded quotient,
 // round-half-even, clamp to the symmetric INT8 range.
 __device__ __forceinline__ int quant_code(float x, float s) {
-    float r = __builtin_rintf(x / s);
-    r = fminf(fmaxf(r, -127.0f), 127.0f);
-    return (int)r;
+    return (int)__builtin_amdgcn_fmed3f(__builtin_rintf(x / s), -127.0f, 127.0f);   // the quotient is finite
 }
 
 // Codes of N values under one non-zero scale s, without a division per value.
@@ -95,18 +93,18 @@ __device__ __forceinline__ void quant_codes(const float (&x)[N], float s, int (&
     for (int e = 0; e < N; ++e) {
         const float t = x[e] * r;
         n[e] = __builtin_rintf(t);
-        near |= fabsf(fabsf(t - n[e]) - 0.5f) < 0x1p-15f;
+        near |= fabsf(t - n[e]) > 0.5f - 0x1p-15f;   // |t - rne(t)| <= 1/2, and the difference is exact
     }
     if (__builtin_amdgcn_ballot_w64(near) != 0) {
 #pragma unroll
         for (int e = 0; e < N; ++e) {
             const float t = x[e] * r;
-            if (fabsf(fabsf(t - n[e]) - 0.5f) < 0x1p-15f) n[e] = __builtin_rintf(x[e] / s);
+            if (fabsf(t - n[e]) > 0.5f - 0x1p-15f) n[e] = __builtin_rintf(x[e] / s);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
 #pragma unroll
-    for (int e = 0; e < N; ++e) code[e] = (int)fminf(fmaxf(n[e], -127.0f), 127.0f);
+    for (int e = 0; e < N; ++e) code[e] = (int)__builtin_amdgcn_fmed3f(n[e], -127.0f, 127.0f);   // n is finite
 }
 
 // Four codes (already in [-127,127]) packed little-endian into one dword.
