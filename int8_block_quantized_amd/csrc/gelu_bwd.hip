@@ -13,7 +13,8 @@
 // Per block, x takes at most 256 values (one per code), so GELU'(x) is
 // evaluated once per code: the four blocks' 256-entry derivative tables are
 // built in binary64 (rounded once to binary32: the definition), x and -x
-// together from one erfc and one exp, and kept in LDS, 1 KiB each.
+// together from one evaluation of the normal tail (jf_gelu.h), and kept in
+// LDS, 1 KiB each.
 // Then per element: dy = fl(sdy*qdy), y = fl(dy * table[qx]), the block max
 // |y| (DPP within rows of 16 lanes, readlanes across them), s = fl(max/127)
 // and the exact codes of quant_codes.
