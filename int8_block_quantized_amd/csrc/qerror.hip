@@ -84,10 +84,13 @@ __global__ __launch_bounds__(64 * kWaves) void k_qe_max(const float *__restrict_
     const int lane = threadIdx.x & (kWave - 1), wave = wave_id_uniform();
     const int band = band0 + blockIdx.y, seg_first = (sg0 + blockIdx.x) * spw;
     float tmax = 0.0f;                                   // tensor: running maximum
+    const int seg_last = min(seg_first + spw, nseg) - 1;
     Tile t = load_tile(x, ldx, nbc, min(seg_first, nseg - 1), band);
 #pragma unroll 1
     for (int j = 0; j < spw && seg_first + j < nseg; ++j) {
-        const Tile nt = load_tile(x, ldx, nbc, min(seg_first + j + 1, nseg - 1), band);   // prefetch
+        // the next segment's loads go out first; after the workgroup's last
+        // segment they re-read it (lines still in L2: no HBM traffic)
+        const Tile nt = load_tile(x, ldx, nbc, min(seg_first + j + 1, seg_last), band);
         if constexpr (G == kTensor) {
 #pragma unroll
             for (int i = 0; i < kRows; ++i)
@@ -216,10 +219,13 @@ __global__ __launch_bounds__(64 * kWaves) void k_qe_err(const float *__restrict_
                                                         double *__restrict__ sse) {
     const int band = band0 + blockIdx.y, seg_first = (sg0 + blockIdx.x) * spw;
     double acc = 0.0;
+    const int seg_last = min(seg_first + spw, nseg) - 1;
     Tile t = load_tile(x, ldx, nbc, min(seg_first, nseg - 1), band);
 #pragma unroll 1
     for (int j = 0; j < spw && seg_first + j < nseg; ++j) {
-        const Tile nt = load_tile(x, ldx, nbc, min(seg_first + j + 1, nseg - 1), band);   // prefetch
+        // the next segment's loads go out first; after the workgroup's last
+        // segment they re-read it (lines still in L2: no HBM traffic)
+        const Tile nt = load_tile(x, ldx, nbc, min(seg_first + j + 1, seg_last), band);
         acc += tile_err<G>(t, s);
         t = nt;
     }
@@ -237,10 +243,13 @@ __global__ __launch_bounds__(64 * kWaves) void k_qe_block(const float *__restric
     const int band = band0 + blockIdx.y, seg_first = (sg0 + blockIdx.x) * spw;
     const int b = lane / 8;
     double acc = 0.0;
+    const int seg_last = min(seg_first + spw, nseg) - 1;
     Tile t = load_tile(x, ldx, nbc, min(seg_first, nseg - 1), band);
 #pragma unroll 1
     for (int j = 0; j < spw && seg_first + j < nseg; ++j) {
-        const Tile nt = load_tile(x, ldx, nbc, min(seg_first + j + 1, nseg - 1), band);   // prefetch
+        // the next segment's loads go out first; after the workgroup's last
+        // segment they re-read it (lines still in L2: no HBM traffic)
+        const Tile nt = load_tile(x, ldx, nbc, min(seg_first + j + 1, seg_last), band);
         float m = 0.0f;
 #pragma unroll
         for (int i = 0; i < kRows; ++i)
