@@ -110,3 +110,28 @@ def test_binary64_derivative_expansion_exhaustive():
     ndiff, worst = int(out[0]), int(out[1])
     note(f"GELU' expansion vs library erfc/exp: {ndiff} of 2^32 outputs differ, by at most {worst} ulp")
     assert worst <= 1 and ndiff <= 2 ** 32 * 1e-7
+
+
+def test_hidden4096_step_shapes_full():
+    """The hidden-4096 bench step's GELU shapes in full: the FC1-output-shaped
+    H (8192 x 16384, 0.5% of columns x100) through GELU, and GELU backward of
+    a gradient of the same shape against H -- every code and scale compared
+    with the oracle."""
+    wl = inputs.hidden4096_block()
+    h, dh = wl.make("H"), wl.make("dH")
+    qh, sh = jf.quantize_block(dev(h))
+    qd, sd = jf.quantize_block(dev(dh))
+    del h, dh
+    note("hidden-4096 GELU / GELU backward: GPU")
+    qg, sg = jf.gelu_i8(qh, sh)
+    qo, so = jf.gelu_bwd_i8(qd, sd, qh, sh)
+    hq, hs, dq, ds = host(qh), host(sh), host(qd), host(sd)
+    gq, gs, bq, bs = host(qg), host(sg), host(qo), host(so)
+    del qh, sh, qd, sd, qg, sg, qo, so
+    note("hidden-4096 GELU / GELU backward: oracle")
+    oq, os_ = oracle.gelu(hq, hs)
+    frac, srel = assert_requant_close(gq, gs, oq, os_, "gelu 8192x16384")
+    note(f"gelu 8192x16384: code diffs {frac:.2e}, scale rel {srel:.1e}")
+    oq, os_ = oracle.gelu_bwd(dq, ds, hq, hs)
+    frac, srel = assert_requant_close(bq, bs, oq, os_, "gelu_bwd 8192x16384")
+    note(f"gelu_bwd 8192x16384: code diffs {frac:.2e}, scale rel {srel:.1e}")
