@@ -1,0 +1,60 @@
+"""The stored fixtures of tests/golden/ (written by tests/golden/make_golden.py
+with the CPU oracle): the oracle still reproduces every stored value bit for
+bit, and the stored quantization satisfies the rule's invariants checked here
+in numpy, independently of the oracle (Jetfire summary, "Approach": one
+scale per 32x32 block, s = max|x|/127, codes rne(x/s) in [-127, 127])."""
+import numpy as np
+
+import oracle
+from golden_io import read
+
+
+def blocks(a):
+    r, c = a.shape
+    return a.reshape(r // 32, 32, c // 32, 32).transpose(0, 2, 1, 3)
+
+
+def test_quantize_fixture():
+    d = read("quantize_32x64.txt")
+    q, s = oracle.quantize(d["x"])
+    np.testing.assert_array_equal(q, d["q"])
+    np.testing.assert_array_equal(s, d["s"])
+    # invariants, in binary64 numpy: the scale is fl(max|x| / 127) of each
+    # block, the block maximum maps to +-127, and |x - s q| <= s/2 up to the
+    # rounding of fl(x / s)
+    xb, qb = blocks(d["x"].astype(np.float64)), blocks(d["q"].astype(np.float64))
+    for i in range(xb.shape[0]):
+        for j in range(xb.shape[1]):
+            m = np.abs(xb[i, j]).max()
+            s_ij = float(d["s"][i, j])
+            assert s_ij == float(np.float32(np.float32(m) / np.float32(127)))
+            assert np.abs(qb[i, j]).max() == 127
+            assert np.all(np.abs(xb[i, j] - s_ij * qb[i, j]) <= s_ij * (0.5 + 2.0 ** -16))
+
+
+def test_gemm_fixture():
+    d = read("gemm_32x32x64.txt")
+    np.testing.assert_array_equal(oracle.gemm_f32(d["a"], d["sa"], d["b"], d["sb"]), d["c"])
+    qc, sc = oracle.gemm_i8(d["a"], d["sa"], d["b"], d["sb"])
+    np.testing.assert_array_equal(qc, d["qc"])
+    np.testing.assert_array_equal(sc, d["sc"])
+    # the F32 result is the scaled integer product up to the fp32 rounding of
+    # the two-term k-block sum (exact rationals bound it)
+    a, b = d["a"].astype(np.float64), d["b"].astype(np.float64)
+    sa, sb = d["sa"].astype(np.float64), d["sb"].astype(np.float64)
+    ref = sum((a[:, 32 * k:32 * k + 32] @ b[32 * k:32 * k + 32]) * float(np.float32(sa[0, k] * sb[k, 0]))
+              for k in range(2))
+    terms = sum(np.abs(a[:, 32 * k:32 * k + 32] @ b[32 * k:32 * k + 32]) * float(np.float32(sa[0, k] * sb[k, 0]))
+                for k in range(2))
+    assert np.all(np.abs(d["c"] - ref) <= terms * 2.0 ** -23)
+
+
+def test_gelu_fixtures():
+    d = read("gelu_32x64.txt")
+    qo, so = oracle.gelu(d["q"], d["s"])
+    np.testing.assert_array_equal(qo, d["qo"])
+    np.testing.assert_array_equal(so, d["so"])
+    d = read("gelu_bwd_32x64.txt")
+    qo, so = oracle.gelu_bwd(d["qdy"], d["sdy"], d["qx"], d["sx"])
+    np.testing.assert_array_equal(qo, d["qo"])
+    np.testing.assert_array_equal(so, d["so"])
