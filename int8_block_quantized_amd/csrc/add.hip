@@ -57,12 +57,10 @@ __global__ __launch_bounds__(256) void k_add_i8(const int8_t *__restrict__ qa, i
                 m = fmaxf(m, fabsf(v));
             }
     }
-    float sbk[kGroupBlocks];
-#pragma unroll
-    for (int bb = 0; bb < kGroupBlocks; ++bb) sbk[bb] = block_scale(group_block_max(m, bb));
+    const float sown = block_scale(group_own_block_max(m));   // the lane's block's output scale
     if (gj0 + b < nbc)
-        store_group_codes(y, pick4(sbk, b), qo + (gi * kBlock + r8) * ldo + (int64_t)(gj0 + b) * kBlock + colb, ldo);
-    if (lane < nb) so[gi * nbc + gj0 + lane] = pick4(sbk, lane);
+        store_group_codes(y, sown, qo + (gi * kBlock + r8) * ldo + (int64_t)(gj0 + b) * kBlock + colb, ldo);
+    if ((lane & 1) == 0 && lane < 2 * nb) so[gi * nbc + gj0 + (lane >> 1)] = sown;   // lanes 0, 2, 4, 6
 }
 
 }  // namespace

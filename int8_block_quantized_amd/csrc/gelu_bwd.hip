@@ -16,8 +16,8 @@
 // together from one evaluation of the normal tail (jf_gelu.h), and kept in
 // LDS, 1 KiB each.
 // Then per element: dy = fl(sdy*qdy), y = fl(dy * table[qx]), the block max
-// |y| (DPP within rows of 16 lanes, readlanes across them), s = fl(max/127)
-// and the exact codes of quant_codes.
+// |y| (DPP within rows of 16 lanes, row-swapping permutes across them),
+// s = fl(max/127) and the exact codes of quant_codes.
 // HBM traffic: 2 bytes in + 1 byte out per element, 12 bytes per block.
 #include "jf_gelu.h"
 #include "jf_group.h"
@@ -105,12 +105,10 @@ __global__ __launch_bounds__(256) void k_gelu_bwd_i8(const int8_t *__restrict__ 
                 m = fmaxf(m, fabsf(v));
             }
     }
-    float sb[kGroup];
-#pragma unroll
-    for (int bb = 0; bb < kGroup; ++bb) sb[bb] = block_scale(group_block_max(m, bb));
+    const float sown = block_scale(group_own_block_max(m));   // the lane's block's output scale
     if (gj0 + b < nbc)
-        store_group_codes(y, pick4(sb, b), qo + (gi * kBlock + r8) * ldo + (int64_t)(gj0 + b) * kBlock + colb, ldo);
-    if (lane < nb) so[gi * nbc + gj0 + lane] = pick4(sb, lane);
+        store_group_codes(y, sown, qo + (gi * kBlock + r8) * ldo + (int64_t)(gj0 + b) * kBlock + colb, ldo);
+    if ((lane & 1) == 0 && lane < 2 * nb) so[gi * nbc + gj0 + (lane >> 1)] = sown;   // lanes 0, 2, 4, 6
 }
 
 }  // namespace

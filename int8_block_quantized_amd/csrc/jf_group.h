@@ -13,16 +13,19 @@ namespace jf {
 
 constexpr int kGroupBlocks = 4;
 
-// Maximum over the 16 lanes holding block b (lanes 8r + 2b + e): DPP over
-// lane bits 0 and 3 within rows of 16, then one readlane per row.  v >= 0,
-// whose IEEE order is the unsigned order of the bits.  Wave-uniform result.
-__device__ __forceinline__ float group_block_max(float v, int b) {
+// Maximum over the 16 lanes holding each block (lanes 8r + 2b + e), in every
+// lane for its own block: DPP over lane bits 0 and 3 within each row of 16
+// lanes, then the gfx950 row-swapping permutes over lane bits 5 and 4.
+// v >= 0, whose IEEE order is the unsigned order of the bits.  Lanes 0, 2, 4
+// and 6 hold blocks 0..3.
+__device__ __forceinline__ float group_own_block_max(float v) {
     uint32_t u = __float_as_uint(v);
     u = max(u, dpp<kDppXor1>(u));
     u = max(u, dpp<kDppRowRor8>(u));
-    const uint32_t a = __builtin_amdgcn_readlane(u, 2 * b), c = __builtin_amdgcn_readlane(u, 16 + 2 * b);
-    const uint32_t d = __builtin_amdgcn_readlane(u, 32 + 2 * b), e = __builtin_amdgcn_readlane(u, 48 + 2 * b);
-    return __uint_as_float(max(max(a, c), max(d, e)));
+    const auto h = __builtin_amdgcn_permlane32_swap(u, u, false, false);   // lanes l and l ^ 32
+    u = max(h[0], h[1]);
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);   // lanes l and l ^ 16
+    return __uint_as_float(max(r[0], r[1]));
 }
 
 // Codes of the lane's 4 x 16 values y (row-major by i) under scale sc,
@@ -44,10 +47,6 @@ __device__ __forceinline__ void store_group_codes(const float (&y)[64], float sc
             u32x4{pack4(code[0], code[1], code[2], code[3]), pack4(code[4], code[5], code[6], code[7]),
                   pack4(code[8], code[9], code[10], code[11]), pack4(code[12], code[13], code[14], code[15])};
     }
-}
-
-__device__ __forceinline__ float pick4(const float (&v)[4], int b) {
-    return b == 0 ? v[0] : b == 1 ? v[1] : b == 2 ? v[2] : v[3];
 }
 
 }  // namespace jf

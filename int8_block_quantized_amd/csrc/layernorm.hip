@@ -178,14 +178,12 @@ __global__ __launch_bounds__(1024) void k_layernorm_i8(const int8_t *__restrict_
                 }
             }
         }
-        float sbk[kGroupBlocks];
-#pragma unroll
-        for (int bb = 0; bb < kGroupBlocks; ++bb) sbk[bb] = block_scale(group_block_max(mx, bb));
+        const float sown = block_scale(group_own_block_max(mx));   // the lane's block's output scale
         const int gj0 = kGroupBlocks * g;
         if (lane_valid(g))
-            store_group_codes(y, pick4(sbk, b), qo + (bi * kBlock + r8) * ldo + (int64_t)(gj0 + b) * kBlock + colb,
-                              ldo);
-        if (lane < min(kGroupBlocks, nbc - gj0)) so[bi * nbc + gj0 + lane] = pick4(sbk, lane);
+            store_group_codes(y, sown, qo + (bi * kBlock + r8) * ldo + (int64_t)(gj0 + b) * kBlock + colb, ldo);
+        if ((lane & 1) == 0 && lane < 2 * min(kGroupBlocks, nbc - gj0))
+            so[bi * nbc + gj0 + (lane >> 1)] = sown;   // lanes 0, 2, 4, 6 hold blocks 0..3
     });
 }
 
