@@ -280,6 +280,44 @@ def bf16_reference(step, steps):
     return ms
 
 
+def int8_library_reference(step, steps):
+    """The same 12 GEMM shapes as plain INT8 GEMMs with int32 output
+    (torch._int_mm, i.e. the vendor BLAS): the contraction alone, with no
+    per-block scales, no rescale and no requantization -- the rate the INT8
+    matrix cores reach through the library, for context.  Random int8
+    operands, A row-major, B column-major (the library's preferred layout)."""
+    import torch
+
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(11)
+    mats = []
+    for kind, label, a in step.ops:
+        if kind != "gemm":
+            continue
+        m = step.meta[label]
+        A = torch.randint(-127, 128, (m["M"], m["K"]), device=dev, generator=g, dtype=torch.int8)
+        B = torch.randint(-127, 128, (m["N"], m["K"]), device=dev, generator=g, dtype=torch.int8).t()
+        mats.append((A, B))
+
+    def run():
+        for A, B in mats:
+            torch._int_mm(A, B)
+
+    run()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        run()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    del mats
+    torch.cuda.empty_cache()
+    return ms
+
+
 def quant_error_section(step, reps=10):
     """jf_quant_error on the step's input activations X (8192 x 4096, outlier
     columns): per scale granularity the mean squared quantization error and
@@ -567,6 +605,18 @@ def main():
                 "int8_gemm_speedup": round(bms / gemm_ms, 3),
                 "what": "the 12 GEMM shapes as torch.mm in bfloat16 (vendor BLAS), operands pre-laid-out, "
                         "bf16 outputs; compared with the INT8 GEMMs' time in the step"}
+    i8lib = None
+    if args.bf16_steps > 0:
+        try:
+            lms = int8_library_reference(step, args.bf16_steps)
+            i8lib = {"ms_per_step": round(lms, 4), "tops": round(step.gemm_ops / (lms * 1e-3) / 1e12, 2),
+                     "frac_of_int8_peak": round(step.gemm_ops / (lms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),
+                     "block_scaled_over_plain_time": round(gemm_ms / lms, 3),
+                     "what": "the 12 GEMM shapes as plain INT8 GEMMs with int32 output (torch._int_mm, vendor "
+                             "BLAS): no block scales, rescale or requantization; the matrix cores' rate for "
+                             "the contraction alone"}
+        except Exception as exc:  # context only, never gating
+            log(f"int8 library reference failed: {exc!r}")
 
     qerr = quant_error_section(step) if args.extras else None
     dfo = data_flow_ops_section(step) if args.extras else None
@@ -604,6 +654,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "bf16_reference": bf16,
+        "int8_library_reference": i8lib,
         "quant_error": qerr,
         "data_flow_ops": dfo,
         "mlp_hidden1024": mlp1024,
