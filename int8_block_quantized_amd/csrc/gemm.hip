@@ -249,7 +249,7 @@ __device__ __forceinline__ void quant_codes_rare(const float (&x)[16], float s, 
         }
     }
 #pragma unroll
-    for (int e = 0; e < 16; ++e) code[e] = (int)fminf(fmaxf(n[e], -127.0f), 127.0f);
+    for (int e = 0; e < 16; ++e) code[e] = (int)__builtin_amdgcn_fmed3f(n[e], -127.0f, 127.0f);   // n is finite
 }
 
 template <int WM, int WN, int GM, int GN, int KB, int S, bool A_KC, bool B_KC, bool OUT_I8, bool NARROW>
