@@ -187,8 +187,8 @@ def read_traffic():
 
 def source_digest() -> str:
     h = hashlib.sha256()
-    for f in ("gemm.hip", "jf_device.h"):
-        h.update(open(os.path.join(ROOT, "int8_block_quantized_amd", "csrc", f), "rb").read())
+    for f in ("csrc/gemm.hip", "csrc/jf_device.h", "_build.py"):   # the kernel and how it is compiled
+        h.update(open(os.path.join(ROOT, "int8_block_quantized_amd", f), "rb").read())
     return h.hexdigest()[:16]
 
 

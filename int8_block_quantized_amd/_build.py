@@ -50,14 +50,41 @@ def build_test_probe(verbose: bool = False) -> list:
     return built
 
 
+# Extra flags for single sources.  gemm.hip: the max-ILP machine scheduler
+# (+1% on the hidden-4096 GEMMs, measured); the same scheduler makes the
+# GELU kernels 14-15% slower, so it is not a library-wide flag.
+PER_SOURCE_FLAGS = {
+    "gemm.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+}
+
+
 def build(verbose: bool = False) -> str:
-    """Compile every HIP source into libjetfire.so (always recompiles)."""
+    """Compile every HIP source into libjetfire.so (always recompiles): one
+    object per source (in parallel), then one shared-library link."""
+    objdir = os.path.join(PKG, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    compile_flags = [f for f in HIPCC_FLAGS if f != "-shared"]
+    procs = []
+    for src in sources():
+        name = os.path.basename(src)
+        obj = os.path.join(objdir, name + ".o")
+        cmd = ["hipcc", *compile_flags, *PER_SOURCE_FLAGS.get(name, []), "-I", os.path.join(ROOT, "include"),
+               "-c", src, "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((cmd, obj, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)))
+    objs = []
+    for cmd, obj, pr in procs:
+        out, err = pr.communicate()
+        if pr.returncode != 0:
+            raise RuntimeError(f"hipcc failed: {' '.join(cmd)}\n{out}\n{err}")
+        objs.append(obj)
     tmp = LIB_PATH + ".tmp"
-    cmd = ["hipcc", *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), *sources(), "-o", tmp]
+    cmd = ["hipcc", "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed:\n{res.stdout}\n{res.stderr}")
+        raise RuntimeError(f"hipcc link failed:\n{res.stdout}\n{res.stderr}")
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
