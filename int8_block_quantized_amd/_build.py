@@ -50,11 +50,14 @@ def build_test_probe(verbose: bool = False) -> list:
     return built
 
 
-# Extra flags for single sources.  gemm.hip: the max-ILP machine scheduler
-# (+1% on the hidden-4096 GEMMs, measured); the same scheduler makes the
-# GELU kernels 14-15% slower, so it is not a library-wide flag.
+# Extra flags for single sources (machine-scheduler strategies, each
+# measured against the default on the same box): gemm.hip max-ILP (+1% on the
+# hidden-4096 GEMMs), quantize.hip max-memory-clause (+1.5% on 16384^2).
+# Neither is library-wide: max-ILP makes the GELU kernels 14-15% slower,
+# max-memory-clause the GELU backward 8% and the residual add 20%.
 PER_SOURCE_FLAGS = {
     "gemm.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+    "quantize.hip": ["-mllvm", "-amdgpu-sched-strategy=max-memory-clause"],
 }
 
 
