@@ -235,3 +235,31 @@ def test_requant_epilogue_ties_and_tiny_scales(ta, tb, scale):
         assert np.all(os_ == 2.0)
         acc = A.astype(np.int64) @ B.astype(np.int64)
         assert (acc % 2 != 0).mean() > 0.3, "too few ties to exercise the rule"
+
+
+@pytest.mark.parametrize("ta,tb", COMBOS)
+@pytest.mark.parametrize("K", [256, 288])
+def test_main_tile_ragged_edges(ta, tb, K):
+    """Grids large enough for the main 128 x 256 tile (33 x 17 = 561 tiles)
+    with a ragged last tile row (one block row of four) and tile column
+    (three block columns of eight); K = 288 has an odd number of k-blocks
+    (one-k-block stages).  F32 output bit-exact and INT8 output exact on the
+    edge blocks and a random sample, all four transposes."""
+    M, N = 4128, 4192
+    A, sA, B, sB, _ = random_operands(60 + K // 32 + 2 * ta + tb, M, N, K, ta, tb)
+    dA, dsA, dB, dsB = dev(A), dev(sA), dev(B), dev(sB)
+    C = host(jf.gemm_i8_blockscaled(dA, dsA, dB, dsB, ta, tb, out="f32"))
+    q, s = jf.gemm_i8_blockscaled(dA, dsA, dB, dsB, ta, tb, out="i8")
+    qh, sh = host(q), host(s)
+    nbM, nbN = M // 32, N // 32
+    blks = sorted(set(sample_blocks(M, N, 24, K + ta + tb)) |
+                  {(nbM - 1, J) for J in range(nbN - 8, nbN)} | {(I, nbN - 1) for I in range(nbM - 4, nbM)})
+    oc = oracle.gemm_f32_blocks(A, sA, B, sB, blks, ta=ta, tb=tb)
+    oq, os_ = oracle.gemm_i8_blocks(A, sA, B, sB, blks, ta=ta, tb=tb)
+    gc = np.stack([C[32 * I:32 * I + 32, 32 * J:32 * J + 32] for I, J in blks])
+    np.testing.assert_array_equal(gc, oc)
+    gq = np.stack([qh[32 * I:32 * I + 32, 32 * J:32 * J + 32] for I, J in blks])
+    gs = np.array([sh[I, J] for I, J in blks])
+    frac, srel = assert_requant_close(gq, gs, oq, os_, f"main tile ragged K={K}")
+    note(f"main-tile ragged {M}x{N}x{K} tA={ta} tB={tb}: {len(blks)} blocks f32 bit-exact, "
+          f"i8 code diffs {frac:.2e}, scale rel {srel:.1e}")
