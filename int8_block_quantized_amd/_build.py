@@ -50,13 +50,14 @@ def build_test_probe(verbose: bool = False) -> list:
     return built
 
 
-# Extra flags for single sources (machine-scheduler strategies, each
-# measured against the default on the same box): gemm.hip max-ILP (+1% on the
-# hidden-4096 GEMMs), quantize.hip max-memory-clause (+1.5% on 16384^2).
+# Extra flags for single sources (machine-scheduler settings, each measured
+# against the alternative on the same box): gemm.hip max-ILP (+1% on the
+# hidden-4096 GEMMs) with the AMDGPU register-pressure trackers (+0.9% more),
+# quantize.hip max-memory-clause (+1.5% on 16384^2).
 # Neither is library-wide: max-ILP makes the GELU kernels 14-15% slower,
 # max-memory-clause the GELU backward 8% and the residual add 20%.
 PER_SOURCE_FLAGS = {
-    "gemm.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+    "gemm.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp", "-mllvm", "-amdgpu-use-amdgpu-trackers=true"],
     "quantize.hip": ["-mllvm", "-amdgpu-sched-strategy=max-memory-clause"],
 }
 
