@@ -51,7 +51,7 @@ def build_test_probe(verbose: bool = False) -> list:
 
 
 # Extra flags for single sources (machine-scheduler settings, each measured
-# against the alternative on the same box): gemm.hip max-ILP (+1% on the
+# against the alternative on the same MI355X): gemm.hip max-ILP (+1% on the
 # hidden-4096 GEMMs) with the AMDGPU register-pressure trackers (+0.9% more),
 # quantize.hip max-memory-clause (+1.5% on 16384^2).
 # Neither is library-wide: max-ILP makes the GELU kernels 14-15% slower,
