@@ -93,9 +93,15 @@ def main():
         out.write(f"    {float.hex(v)},  // t^{i}\n")
     out.write("};\n\n")
     out.write(
-        "// M(z) = Q(z) exp(z^2/2) for z >= 0 (finite): one division, Horner in t.\n"
+        "// M(z) = Q(z) exp(z^2/2) for z >= 0 (finite): a reciprocal, Horner in t.\n"
+        "// w = 1/(z + K) from the hardware estimate and two Newton steps (each\n"
+        "// squares the relative error, so w is within an ulp of the quotient),\n"
+        "// not an IEEE division: a few ulps in t move M by ~1e-16 relative.\n"
         "__device__ __forceinline__ double normal_tail_scaled(double z) {\n"
-        "    const double w = 1.0 / (z + kTailK);\n"
+        "    const double d = z + kTailK;\n"
+        "    double w = __builtin_amdgcn_rcp(d);\n"
+        "    w = __builtin_fma(w, __builtin_fma(-d, w, 1.0), w);\n"
+        "    w = __builtin_fma(w, __builtin_fma(-d, w, 1.0), w);\n"
         "    const double t = (z - kTailK) * w;\n"
         "    double p = kTailPoly[kTailDegree];\n"
         "#pragma unroll\n"

@@ -39,9 +39,15 @@ __device__ constexpr double kTailPoly[kTailDegree + 1] = {
     0x1.828df1c3afaadp-34,  // t^24
 };
 
-// M(z) = Q(z) exp(z^2/2) for z >= 0 (finite): one division, Horner in t.
+// M(z) = Q(z) exp(z^2/2) for z >= 0 (finite): a reciprocal, Horner in t.
+// w = 1/(z + K) from the hardware estimate and two Newton steps (each
+// squares the relative error, so w is within an ulp of the quotient),
+// not an IEEE division: a few ulps in t move M by ~1e-16 relative.
 __device__ __forceinline__ double normal_tail_scaled(double z) {
-    const double w = 1.0 / (z + kTailK);
+    const double d = z + kTailK;
+    double w = __builtin_amdgcn_rcp(d);
+    w = __builtin_fma(w, __builtin_fma(-d, w, 1.0), w);
+    w = __builtin_fma(w, __builtin_fma(-d, w, 1.0), w);
     const double t = (z - kTailK) * w;
     double p = kTailPoly[kTailDegree];
 #pragma unroll

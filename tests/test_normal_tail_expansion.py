@@ -2,9 +2,10 @@
 the upper normal tail that the INT8 GELU backward kernel uses for GELU').
 
 M(z) = Q(z) exp(z^2/2), Q the upper normal tail, is evaluated from the
-header's power-basis coefficients in t = (z - K)/(z + K) exactly as the
-kernel does (binary64 Horner), and compared with 50-digit mpmath: relative
-error below 1e-15 on [0, 40].  The GELU' pair built from it must round to the
+header's power-basis coefficients in t = (z - K)/(z + K) with binary64
+Horner as the kernel does (here with an IEEE division for 1/(z + K); the
+kernel's Newton-refined reciprocal is within an ulp of it), and compared
+with 50-digit mpmath: relative error below 1e-15 on [0, 40].  The GELU' pair built from it must round to the
 correctly rounded binary32 values of Phi(x) + x phi(x) (50-digit mpmath) on a
 seeded sample of inputs and at the special points x = 0, the zero of GELU'
 near -0.7518 and the tails.
