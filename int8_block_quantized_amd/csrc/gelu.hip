@@ -43,14 +43,16 @@
 namespace jf {
 namespace {
 
-// gelu_ref as a call: one copy of the binary64 code instead of one per use,
-// and its constants stay out of the kernel's loop registers.
-__device__ __attribute__((noinline)) float gelu_ref_outlined(float x) { return gelu_ref(x); }
+// The binary64 reference value (gelu_tail: the normal-tail expansion, 66
+// VALU instructions against 144 for the library erfc) as a call: one copy of
+// the code instead of one per use, and its registers stay out of the
+// kernel's loop.
+__device__ __attribute__((noinline)) float gelu_ref_outlined(float x) { return gelu_tail(x); }
 
 // Output codes of a lane's table entries.  g holds gelu_fast values, s2 =
-// fl(m/127) with m = gelu_ref of the block's largest code, m >= 0.17, so the
+// fl(m/127) with m = gelu_tail of the block's largest code, m >= 0.17, so the
 // table inputs satisfy |x| >= 0.0022 or x = 0, where gelu_fast is within
-// 6.51e-7 |gref| of gref = gelu_ref(x) for x >= 0 and within 2.14e-7 of it
+// 6.51e-7 |gref| of gref = gelu_tail(x) for x >= 0 and within 2.14e-7 of it
 // for x < 0.  Let r = rcp(s2) (hardware reciprocal, within one ulp, i.e.
 // 2^-23 relative), t = fl(g r) and Q = fl(gref / s2), the quotient whose
 // rne is the reference code.  Collecting the reciprocal's error and the two
@@ -61,7 +63,7 @@ __device__ __attribute__((noinline)) float gelu_ref_outlined(float x) { return g
 // w away from the nearest half-integer (t - rne(t) is exact); the test uses
 // w + 2^-20, which covers its own roundings.  The other entries (about
 // 1.5e-4 of the positive ones at the bench input's scales, far fewer of the
-// negative ones) are recomputed from gelu_ref with an IEEE division, one
+// negative ones) are recomputed from gelu_tail with an IEEE division, one
 // wavefront-wide binary64 call per round.
 template <int N>
 __device__ __forceinline__ void table_codes(const float (&g)[N], const float (&x)[N], float s2, int (&code)[N]) {

@@ -107,6 +107,51 @@ def main():
         "#pragma unroll\n"
         "    for (int k = kTailDegree - 1; k >= 0; --k) p = __builtin_fma(p, t, kTailPoly[k]);\n"
         "    return p * (kTailK * w);\n"
+        "}\n\n")
+    # e^{-u}: Cody-Waite reduction by ln 2 (a high part with 21 trailing zero
+    # bits, so k * hi is exact for |k| < 2^21, and the low part), then the Taylor
+    # polynomial of degree 13 on |r| <= ln2/2 (truncation below 4e-18 relative)
+    hi = float.fromhex("0x1.62e42feep-1")
+    lo = float(mp.log(2) - mp.mpf(hi))
+    inv_fact = [float(1 / mp.factorial(n)) for n in range(13, -1, -1)]
+    out.write(
+        "// Forces a constant into scalar registers, so that a binary64 FMA takes it\n"
+        "// as an operand (a literal would cost two VALU moves at each use outside a\n"
+        "// loop the compiler can hoist it from).\n"
+        "__device__ __forceinline__ double sreg(double c) {\n"
+        "    __asm__(\"\" : \"+s\"(c));\n"
+        "    return c;\n"
+        "}\n\n")
+    out.write(f"constexpr double kExpLn2Hi = {float.hex(hi)}, kExpLn2Lo = {float.hex(lo)};\n")
+    out.write("constexpr double kExpInvFact[14] = {   // 1/13!, 1/12!, ..., 1/1!, 1/0!\n")
+    for i, v in enumerate(inv_fact):
+        out.write(f"    {float.hex(v)},\n")
+    out.write("};\n\n")
+    out.write(
+        "// e^{-u} for u >= 0 with the constants in scalar registers: k = rne(u / ln 2),\n"
+        "// r = u - k ln 2 (two FMAs), e^{-u} = 2^-k e^{-r}.  u is capped at 746, where\n"
+        "// e^{-u} already rounds to 0 (and k stays far inside the int range).\n"
+        "__device__ __forceinline__ double exp_neg_s(double u) {\n"
+        "    u = __builtin_fmin(u, 746.0);\n"
+        "    const double k = __builtin_rint(u * 1.4426950408889634074);\n"
+        "    const double r = __builtin_fma(-k, sreg(kExpLn2Lo), __builtin_fma(-k, sreg(kExpLn2Hi), u));\n"
+        "    double p = sreg(kExpInvFact[0]);\n"
+        "#pragma unroll\n"
+        "    for (int i = 1; i < 14; ++i) p = __builtin_fma(p, -r, sreg(kExpInvFact[i]));\n"
+        "    return __builtin_amdgcn_ldexp(p, -(int)k);\n"
+        "}\n\n"
+        "// normal_tail_scaled with the polynomial's constants in scalar registers\n"
+        "// (for a call made once per wavefront, outside any loop).\n"
+        "__device__ __forceinline__ double normal_tail_scaled_s(double z) {\n"
+        "    const double d = z + kTailK;\n"
+        "    double w = __builtin_amdgcn_rcp(d);\n"
+        "    w = __builtin_fma(w, __builtin_fma(-d, w, 1.0), w);\n"
+        "    w = __builtin_fma(w, __builtin_fma(-d, w, 1.0), w);\n"
+        "    const double t = (z - kTailK) * w;\n"
+        "    double p = sreg(kTailPoly[kTailDegree]);\n"
+        "#pragma unroll\n"
+        "    for (int k = kTailDegree - 1; k >= 0; --k) p = __builtin_fma(p, t, sreg(kTailPoly[k]));\n"
+        "    return p * (kTailK * w);\n"
         "}\n\n}  // namespace jf\n")
 
 

@@ -20,6 +20,18 @@ __device__ __forceinline__ float gelu_ref(float x) {
     return (float)(xd * (0.5 * erfc(-xd * 0.70710678118654752440)));
 }
 
+// The same value from the normal-tail expansion (jf_normal_tail.h), with
+// every constant in scalar registers: the INT8 GELU kernel evaluates it once
+// per wavefront (its blocks' largest values) and in rare fallbacks, through
+// a call, where the library erfc's constants cost about 60 VALU moves.
+// Phi(x) = 1 - Q(x) for x >= 0 and Q(-x) for x < 0, Q(z) = e^{-z^2/2} M(z);
+// z*z is exact in binary64.
+__device__ __forceinline__ float gelu_tail(float x) {
+    const double xd = (double)x, z = fabs(xd);
+    const double q = exp_neg_s(0.5 * (z * z)) * normal_tail_scaled_s(z);
+    return (float)(xd * (xd >= 0.0 ? 1.0 - q : q));
+}
+
 // GELU'(z) (.x) and GELU'(-z) (.y) for z >= 0 in binary64 from the
 // normal-tail expansion of jf_normal_tail.h (one exp, one division and a
 // degree-24 polynomial: about a third of the instructions of the library's

@@ -55,4 +55,57 @@ __device__ __forceinline__ double normal_tail_scaled(double z) {
     return p * (kTailK * w);
 }
 
+// Forces a constant into scalar registers, so that a binary64 FMA takes it
+// as an operand (a literal would cost two VALU moves at each use outside a
+// loop the compiler can hoist it from).
+__device__ __forceinline__ double sreg(double c) {
+    __asm__("" : "+s"(c));
+    return c;
+}
+
+constexpr double kExpLn2Hi = 0x1.62e42fee00000p-1, kExpLn2Lo = 0x1.a39ef35793c76p-33;
+constexpr double kExpInvFact[14] = {   // 1/13!, 1/12!, ..., 1/1!, 1/0!
+    0x1.6124613a86d09p-33,
+    0x1.1eed8eff8d898p-29,
+    0x1.ae64567f544e4p-26,
+    0x1.27e4fb7789f5cp-22,
+    0x1.71de3a556c734p-19,
+    0x1.a01a01a01a01ap-16,
+    0x1.a01a01a01a01ap-13,
+    0x1.6c16c16c16c17p-10,
+    0x1.1111111111111p-7,
+    0x1.5555555555555p-5,
+    0x1.5555555555555p-3,
+    0x1.0000000000000p-1,
+    0x1.0000000000000p+0,
+    0x1.0000000000000p+0,
+};
+
+// e^{-u} for u >= 0 with the constants in scalar registers: k = rne(u / ln 2),
+// r = u - k ln 2 (two FMAs), e^{-u} = 2^-k e^{-r}.  u is capped at 746, where
+// e^{-u} already rounds to 0 (and k stays far inside the int range).
+__device__ __forceinline__ double exp_neg_s(double u) {
+    u = __builtin_fmin(u, 746.0);
+    const double k = __builtin_rint(u * 1.4426950408889634074);
+    const double r = __builtin_fma(-k, sreg(kExpLn2Lo), __builtin_fma(-k, sreg(kExpLn2Hi), u));
+    double p = sreg(kExpInvFact[0]);
+#pragma unroll
+    for (int i = 1; i < 14; ++i) p = __builtin_fma(p, -r, sreg(kExpInvFact[i]));
+    return __builtin_amdgcn_ldexp(p, -(int)k);
+}
+
+// normal_tail_scaled with the polynomial's constants in scalar registers
+// (for a call made once per wavefront, outside any loop).
+__device__ __forceinline__ double normal_tail_scaled_s(double z) {
+    const double d = z + kTailK;
+    double w = __builtin_amdgcn_rcp(d);
+    w = __builtin_fma(w, __builtin_fma(-d, w, 1.0), w);
+    w = __builtin_fma(w, __builtin_fma(-d, w, 1.0), w);
+    const double t = (z - kTailK) * w;
+    double p = sreg(kTailPoly[kTailDegree]);
+#pragma unroll
+    for (int k = kTailDegree - 1; k >= 0; --k) p = __builtin_fma(p, t, sreg(kTailPoly[k]));
+    return p * (kTailK * w);
+}
+
 }  // namespace jf

@@ -84,3 +84,67 @@ def test_pair_rounds_like_the_exact_derivative():
     assert bad == 0, bad
     assert pair_header(np.float32(0), k, a) == (np.float32(0.5), np.float32(0.5))
 
+
+
+def exp_constants():
+    text = open(HDR).read()
+    hi = float.fromhex(re.search(r"kExpLn2Hi = (-?0x[0-9a-fp.+-]+)", text).group(1))
+    lo = float.fromhex(re.search(r"kExpLn2Lo = (-?0x[0-9a-fp.+-]+)", text).group(1))
+    body = text[text.index("kExpInvFact[14]"):]
+    body = body[:body.index("};")]
+    inv = [float.fromhex(c) for c in re.findall(r"^\s+(-?0x[0-9a-fp.+-]+),$", body, re.M)]
+    assert len(inv) == 14
+    return hi, lo, inv
+
+
+def fma(a, b, c):
+    return float(mp.mpf(a) * mp.mpf(b) + mp.mpf(c))
+
+
+def exp_neg_header(u, hi, lo, inv):
+    u = min(u, 746.0)
+    k = float(round(u * 1.4426950408889634074))      # round half to even, like rint
+    r = fma(-k, lo, fma(-k, hi, u))
+    p = inv[0]
+    for c in inv[1:]:
+        p = fma(p, -r, c)
+    return float(mp.ldexp(mp.mpf(p), -int(k)))
+
+
+def test_exp_reduction_constants():
+    """ln 2 split (the high part with 21 trailing zero bits, so k*hi is exact
+    for |k| < 2^21; k <= 1077 here), 1/n! rounded once, and e^{-u} from them within 2 binary64
+    ulps of 50-digit exp on [0, 700] (FMAs emulated exactly)."""
+    mp.mp.dps = 50
+    hi, lo, inv = exp_constants()
+    assert abs(mp.mpf(hi) + mp.mpf(lo) - mp.log(2)) < mp.mpf(2) ** -80
+    assert (np.float64(hi).view(np.uint64) & np.uint64((1 << 21) - 1)) == 0   # low 21 mantissa bits zero
+    for i, v in enumerate(inv):
+        assert v == float(1 / mp.factorial(13 - i))
+    g = np.random.default_rng(9)
+    us = list(g.uniform(0, 120, 400)) + list(g.uniform(0, 1, 200)) + [0.0, 0.3465, 0.3466, 30.1656, 700.0]
+    worst = max(float(abs(mp.mpf(exp_neg_header(float(u), hi, lo, inv)) - mp.exp(-mp.mpf(float(u)))) /
+                      mp.exp(-mp.mpf(float(u)))) for u in us)
+    assert worst < 2 * 2.0 ** -53, worst
+    assert exp_neg_header(800.0, hi, lo, inv) == 0.0
+
+
+def test_gelu_value_rounds_like_the_exact_value():
+    """The forward kernel's binary64 reference GELU (x Phi(x) from the tail
+    expansion and the exp above) rounds to the correctly rounded binary32
+    value of 50-digit x Phi(x) on a seeded sample and at special points."""
+    mp.mp.dps = 50
+    k, a = header_constants()
+    hi, lo, inv = exp_constants()
+    g = np.random.default_rng(8)
+    xs = np.concatenate([g.uniform(-15, 15, 1200), 10 ** g.uniform(-7, 1.1, 250),
+                         -(10 ** g.uniform(-7, 1.1, 250)), [0.0, -0.7518, 5.9, -5.9, -14.0, 30.0, 1e4]]).astype(np.float32)
+    bad = 0
+    for x in xs:
+        xd = float(x)
+        z = abs(xd)
+        q = exp_neg_header(0.5 * z * z, hi, lo, inv) * m_header(z, k, a)
+        got = np.float32(xd * (1.0 - q if xd >= 0 else q))
+        xm = mp.mpf(xd)
+        bad += int(got != to_f32(xm * mp.erfc(-xm / mp.sqrt(2)) / 2))
+    assert bad == 0, bad
