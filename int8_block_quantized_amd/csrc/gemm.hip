@@ -47,6 +47,7 @@
 
 #include "jf_device.h"
 #include "jf_launch.h"
+#include "jf_tile_order.h"
 
 #ifndef JF_GEMM_WM
 #define JF_GEMM_WM 2
@@ -68,6 +69,19 @@
 #endif
 #ifndef JF_GEMM_PIPE
 #define JF_GEMM_PIPE 0
+#endif
+// Partial conversion through the MFMA's C operand (see rescale below).
+#ifndef JF_GEMM_BIAS
+#define JF_GEMM_BIAS 0
+#endif
+// 1: every k-block's fragments of a stage are read before its first MFMA;
+// 0: k-block kk+1's fragments are read after k-block kk's last MFMA issues.
+#ifndef JF_GEMM_FRAG_EARLY
+#define JF_GEMM_FRAG_EARLY 1
+#endif
+// Scale prefetch: the next stage's scales are loaded during this stage.
+#ifndef JF_GEMM_SPREF
+#define JF_GEMM_SPREF 0
 #endif
 // Smaller tile for grids that would leave SIMDs with one wavefront or none:
 // used when the main tile gives fewer than JF_GEMM_SMALL_BELOW workgroups.
@@ -270,23 +284,9 @@ __global__ __launch_bounds__(64 * GM * GN) JF_GEMM_OCCUPANCY void k_gemm_i8bs(
     const int wave = wave_id_uniform();
     const int wr = wave / GN, wc = wave % GN;
 
-    // Tile order.  Workgroups are dealt to the eight XCDs round-robin
-    // (XCD = blockIdx % 8), each with its own L2: renumber so that every XCD
-    // owns one contiguous range of tiles, and walk that range in groups of
-    // eight tile rows so neighbouring workgroups share A and B panels.
-    int tm, tn;
-    {
-        const int ntiles = gridDim.x, tilesM = ntiles / tilesN;
-        const int bid = blockIdx.x, x = bid % 8, j = bid / 8;
-        const int per = ntiles / 8, rem = ntiles % 8;
-        const int t = x * per + min(x, rem) + j;
-        constexpr int kGroup = 8;
-        const int in_group = kGroup * tilesN;
-        const int first_m = (t / in_group) * kGroup;
-        const int gsize = min(tilesM - first_m, kGroup);
-        tm = first_m + (t % in_group) % gsize;
-        tn = (t % in_group) / gsize;
-    }
+    // Tile order: XCD-aware renumbering (jf_tile_order.h).
+    const TileCoord tc = tile_of(blockIdx.x, gridDim.x, tilesN);
+    const int tm = tc.tm, tn = tc.tn;
     const int row0 = tm * BM, col0 = tn * BN;
     const int nbM = M / kBlock, nbN = N / kBlock, nkb = K / kBlock;
     const int I0 = row0 / kBlock + wr * WM, J0 = col0 / kBlock + wc * WN;
@@ -342,9 +342,35 @@ __global__ __launch_bounds__(64 * GM * GN) JF_GEMM_OCCUPANCY void k_gemm_i8bs(
     static_for<S - 1>([&](auto p) {
         if (decltype(p)::value < nstage) issue(p);
     });
+    // Scales of the current stage, loaded one stage ahead (JF_GEMM_SPREF):
+    // the scalar loads are issued after the stage's fragment reads have been
+    // waited for, so that wait (lgkmcnt, shared by LDS and scalar loads)
+    // never covers a scale load still in flight.
+    const float *sA0[WM], *sB0[WN];
+#pragma unroll
+    for (int a = 0; a < WM; ++a) sA0[a] = pA[a];
+#pragma unroll
+    for (int b = 0; b < WN; ++b) sB0[b] = pB[b];
+    float csa[KB][WM], csb[KB][WN];
+    auto load_scales = [&](int stg) {
+        const int64_t k0 = (int64_t)min(stg, nstage - 1) * KB;
+#pragma unroll
+        for (int kk = 0; kk < KB; ++kk) {
+#pragma unroll
+            for (int a = 0; a < WM; ++a) csa[kk][a] = sA0[a][(k0 + kk) * stepA];
+#pragma unroll
+            for (int b = 0; b < WN; ++b) csb[kk][b] = sB0[b][(k0 + kk) * stepB];
+        }
+    };
+    if constexpr (JF_GEMM_SPREF) load_scales(0);
 
     constexpr int NB = WM * WN, T = KB * NB;
     constexpr bool kPipe = JF_GEMM_PIPE;
+    constexpr bool kBias = JF_GEMM_BIAS;
+    constexpr float kBiasF = 12582912.0f;   // 1.5 * 2^23, bits 0x4B400000
+    v16i bias;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) bias[r] = 0x4B400000;
     // One stage; SLOT = st % S is a compile-time constant (the loop below is
     // unrolled by S), so every LDS address is a per-lane base plus an
     // immediate offset.
@@ -392,9 +418,23 @@ __global__ __launch_bounds__(64 * GM * GN) JF_GEMM_OCCUPANCY void k_gemm_i8bs(
 #pragma unroll
                 for (int b = 0; b < WN; ++b) sg[a][b] = sa[a] * sb[b];
         };
+        // With the bias, the MFMA adds the partial to C = bits of 1.5 * 2^23
+        // (integer addition): for |P| < 2^22 the sum's bits are exactly the
+        // binary32 number 1.5 * 2^23 + P (same exponent, P added to the
+        // significand), and |P| <= 32 * 127^2 = 516128.  Subtracting 1.5 * 2^23
+        // is then exact (Sterbenz) and yields (float)P: one add, at twice the
+        // issue rate of v_cvt_f32_i32.  Either way the fma gets the same value.
+        auto mfma = [&](const v4i &b, const v4i &a) {
+            if constexpr (kBias) return __builtin_amdgcn_mfma_i32_32x32x32_i8(b, a, bias, 0, 0, 0);
+            else return __builtin_amdgcn_mfma_i32_32x32x32_i8(b, a, v16i{}, 0, 0, 0);
+        };
         auto rescale = [&](float (&acc_b)[16], float sigma, const v16i &p) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc_b[r] = __builtin_fmaf(sigma, (float)p[r], acc_b[r]);
+            for (int r = 0; r < 16; ++r) {
+                const int pr = p[r];   // (a bit_cast of the vector element itself reads element 0)
+                const float pf = kBias ? __int_as_float(pr) - kBiasF : (float)pr;
+                acc_b[r] = __builtin_fmaf(sigma, pf, acc_b[r]);
+            }
         };
         if constexpr (kPipe) {
             v4i af[KB][WM], bf[KB][WN];
@@ -407,22 +447,58 @@ __global__ __launch_bounds__(64 * GM * GN) JF_GEMM_OCCUPANCY void k_gemm_i8bs(
             // pairs: the MFMA of pair t+1 is issued before the rescale of
             // pair t, so the matrix core works while the VALU converts and
             // accumulates.
-            v16i pc = __builtin_amdgcn_mfma_i32_32x32x32_i8(bf[0][0], af[0][0], v16i{}, 0, 0, 0);
+            v16i pc = mfma(bf[0][0], af[0][0]);
 #pragma unroll
             for (int t = 0; t < T; ++t) {
                 const int kk = t / NB, a = (t % NB) / WN, b = t % WN;
-                float sigma = sg[kk][a][b];
                 v16i pn;
                 if (t + 1 < T) {
                     const int kn = (t + 1) / NB, an = ((t + 1) % NB) / WN, bn = (t + 1) % WN;
-                    pn = __builtin_amdgcn_mfma_i32_32x32x32_i8(bf[kn][bn], af[kn][an], v16i{}, 0, 0, 0);
-                    // keeps the next MFMA ahead of this rescale in the schedule
-                    asm volatile("; mfma before rescale" : "+v"(sigma) : "v"(pn));
+                    pn = mfma(bf[kn][bn], af[kn][an]);
                 }
-                rescale(acc[a][b], sigma, pc);
+                // the next MFMA stays ahead of this rescale in the schedule
+                __builtin_amdgcn_sched_barrier(0);
+                rescale(acc[a][b], sg[kk][a][b], pc);
+                __builtin_amdgcn_sched_barrier(0);
                 if (t + 1 < T) pc = pn;
             }
-        } else {
+        } else if constexpr (JF_GEMM_FRAG_EARLY && JF_GEMM_SPREF) {
+            // Scale products from the prefetched scales first (their loads
+            // were issued a stage ago), then every fragment of the stage.
+            float sg[KB][WM][WN];
+#pragma unroll
+            for (int kk = 0; kk < KB; ++kk)
+#pragma unroll
+                for (int a = 0; a < WM; ++a)
+#pragma unroll
+                    for (int b = 0; b < WN; ++b) sg[kk][a][b] = csa[kk][a] * csb[kk][b];
+            __builtin_amdgcn_sched_barrier(0);
+            v4i af[KB][WM], bf[KB][WN];
+#pragma unroll
+            for (int kk = 0; kk < KB; ++kk) {
+#pragma unroll
+                for (int a = 0; a < WM; ++a) af[kk][a] = TA::frag(la, wr * WM + a, kk, lane);
+#pragma unroll
+                for (int b = 0; b < WN; ++b) bf[kk][b] = TB::frag(lb, wc * WN + b, kk, lane);
+            }
+            if (st + S - 1 < nstage) issue(std::integral_constant<int, (SLOT + S - 1) % S>{});
+#pragma unroll
+            for (int kk = 0; kk < KB; ++kk)
+#pragma unroll
+                for (int a = 0; a < WM; ++a)
+#pragma unroll
+                    for (int b = 0; b < WN; ++b) {
+                        const v16i p = mfma(bf[kk][b], af[kk][a]);
+                        rescale(acc[a][b], sg[kk][a][b], p);
+                        __builtin_amdgcn_sched_barrier(0);
+                        if (kk == 0 && a == 0 && b == 0) {
+                            // every fragment read of the stage has been waited
+                            // for by now (the first MFMA needed them)
+                            load_scales(st + 1);
+                            __builtin_amdgcn_sched_barrier(0);
+                        }
+                    }
+        } else if constexpr (JF_GEMM_FRAG_EARLY) {
             // Every k-block's fragments and scale products of the stage are
             // read first (the later k-blocks' LDS reads overlap the first
             // k-block's MFMAs), then each MFMA is followed by its rescale.
@@ -437,8 +513,35 @@ __global__ __launch_bounds__(64 * GM * GN) JF_GEMM_OCCUPANCY void k_gemm_i8bs(
                 for (int a = 0; a < WM; ++a)
 #pragma unroll
                     for (int b = 0; b < WN; ++b) {
-                        const v16i p = __builtin_amdgcn_mfma_i32_32x32x32_i8(bf[kk][b], af[kk][a], v16i{}, 0, 0, 0);
+                        const v16i p = mfma(bf[kk][b], af[kk][a]);
                         rescale(acc[a][b], sg[kk][a][b], p);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+        } else {
+            // One k-block's fragments at a time: those of k-block kk+1 are
+            // read into the same registers once k-block kk's last MFMA has
+            // taken its operands, and arrive during that MFMA's rescale.
+            v4i af[WM], bf[WN];
+            float sg[WM][WN];
+            load_kk(0, af, bf, sg);
+            if (st + S - 1 < nstage) issue(std::integral_constant<int, (SLOT + S - 1) % S>{});
+#pragma unroll
+            for (int kk = 0; kk < KB; ++kk)
+#pragma unroll
+                for (int a = 0; a < WM; ++a)
+#pragma unroll
+                    for (int b = 0; b < WN; ++b) {
+                        const v16i p = mfma(bf[b], af[a]);
+                        const float sigma = sg[a][b];
+                        if (a == WM - 1 && b == WN - 1 && kk + 1 < KB) {
+                            float sg_n[WM][WN];
+                            load_kk(kk + 1, af, bf, sg_n);
+#pragma unroll
+                            for (int i = 0; i < WM; ++i)
+#pragma unroll
+                                for (int j = 0; j < WN; ++j) sg[i][j] = sg_n[i][j];
+                        }
+                        rescale(acc[a][b], sigma, p);
                         __builtin_amdgcn_sched_barrier(0);
                     }
         }

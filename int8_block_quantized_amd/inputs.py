@@ -65,6 +65,17 @@ def scales(workload_id: int, tag: int, index: int, rows: int, cols: int) -> np.n
     return (mant * 10.0 ** g.integers(-4, -1, size=(rows, cols))).astype(np.float32)
 
 
+def small_codes(workload_id: int, tag: int, index: int, rows: int, cols: int, qmax: int) -> np.ndarray:
+    """Uniform int8 codes in [-qmax, qmax]."""
+    return rng(workload_id, tag, index).integers(-qmax, qmax + 1, size=(rows, cols)).astype(np.int8)
+
+
+def pow2_scales(workload_id: int, tag: int, index: int, rows: int, cols: int, emin: int, emax: int) -> np.ndarray:
+    """float32 powers of two 2^e with e uniform in [emin, emax]."""
+    e = rng(workload_id, tag, index).integers(emin, emax + 1, size=(rows, cols))
+    return np.ldexp(np.ones((rows, cols), np.float32), e).astype(np.float32)
+
+
 def n_outliers(fraction: float, cols: int) -> int:
     return int(round(fraction * cols))
 

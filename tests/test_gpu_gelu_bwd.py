@@ -135,3 +135,52 @@ def test_hidden4096_step_shapes_full():
     oq, os_ = oracle.gelu_bwd(dq, ds, hq, hs)
     frac, srel = assert_requant_close(bq, bs, oq, os_, "gelu_bwd 8192x16384")
     note(f"gelu_bwd 8192x16384: code diffs {frac:.2e}, scale rel {srel:.1e}")
+
+
+def test_mlp_backward_chain_fc2_dgrad_gelu_bwd_fc1():
+    """The GPT2-medium MLP backward data flow end to end, all INT8 with
+    per-block scales: FC2 activation gradient (dG = dY2 . W2^T, the gradient
+    at the GELU output), GELU backward (dH = dG * GELU'(H), H the FC1 output),
+    then FC1's activation gradient (dX = dH . W1^T) and weight gradient
+    (dW1 = X^T . dH).  The oracle runs the same chain from the raw fp32
+    inputs; every intermediate is compared in full, dX on three row strips and
+    dW1 on every 8th block row (the oracle needs all of dH for each)."""
+    wl = inputs.gpt2_medium_mlp()
+    x, w1, w2, dy2 = wl.make("X"), wl.make("W1"), wl.make("W2"), wl.make("dY2")
+    note("mlp backward chain: GPU")
+    qx, sx = jf.quantize_block(dev(x))
+    qw1, sw1 = jf.quantize_block(dev(w1))
+    qw2, sw2 = jf.quantize_block(dev(w2))
+    qdy, sdy = jf.quantize_block(dev(dy2))
+    qh, sh = jf.gemm_i8_blockscaled(qx, sx, qw1, sw1)               # FC1 forward (GELU input) 8192 x 4096
+    qg, sg = jf.gemm_i8_blockscaled(qdy, sdy, qw2, sw2, 0, 1)       # FC2 dgrad 8192 x 4096
+    qd, sd = jf.gelu_bwd_i8(qg, sg, qh, sh)                         # GELU backward
+    qdx, sdx = jf.gemm_i8_blockscaled(qd, sd, qw1, sw1, 0, 1)       # FC1 dgrad 8192 x 1024
+    qdw, sdw = jf.gemm_i8_blockscaled(qx, sx, qd, sd, 1, 0)         # FC1 wgrad 1024 x 4096
+    got = {k: (host(a), host(b)) for k, (a, b) in
+           {"H": (qh, sh), "dG": (qg, sg), "dH": (qd, sd), "dX": (qdx, sdx), "dW1": (qdw, sdw)}.items()}
+    note("mlp backward chain: oracle")
+    oqx, osx = oracle.quantize(x)
+    oqw1, osw1 = oracle.quantize(w1)
+    oqw2, osw2 = oracle.quantize(w2)
+    oqdy, osdy = oracle.quantize(dy2)
+    ref = {"H": oracle.gemm_i8(oqx, osx, oqw1, osw1),
+           "dG": oracle.gemm_i8(oqdy, osdy, oqw2, osw2, ta=0, tb=1)}
+    ref["dH"] = oracle.gelu_bwd(*ref["dG"], *ref["H"])
+    for k in ("H", "dG", "dH"):
+        frac, srel = assert_requant_close(*got[k], *ref[k], f"chain {k}")
+        note(f"  {k}: code diffs {frac:.2e}, scale rel {srel:.1e}")
+    odq, ods = ref["dH"]
+    for I in (0, 101, 255):
+        blks = [(I, J) for J in range(1024 // 32)]
+        bq, bs = oracle.gemm_i8_blocks(odq, ods, oqw1, osw1, blks, ta=0, tb=1)
+        gq = got["dX"][0][32 * I:32 * I + 32].reshape(32, 32, 32).transpose(1, 0, 2)
+        frac, srel = assert_requant_close(gq, got["dX"][1][I], bq, bs, f"chain dX strip {I}")
+        note(f"  dX strip {I}: code diffs {frac:.2e}, scale rel {srel:.1e}")
+    rows = list(range(0, 1024 // 32, 8))
+    blks = [(I, J) for I in rows for J in range(4096 // 32)]
+    bq, bs = oracle.gemm_i8_blocks(oqx, osx, odq, ods, blks, ta=1, tb=0)
+    gq = np.stack([got["dW1"][0][32 * I:32 * I + 32, 32 * J:32 * J + 32] for I, J in blks])
+    gs = np.array([got["dW1"][1][I, J] for I, J in blks])
+    frac, srel = assert_requant_close(gq, gs, bq, bs, "chain dW1")
+    note(f"  dW1 block rows {rows}: code diffs {frac:.2e}, scale rel {srel:.1e}")

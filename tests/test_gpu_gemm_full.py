@@ -1,0 +1,178 @@
+"""GPU parity of the block-scaled GEMM over whole outputs and at full size.
+
+1. Main tile, every element.  Grids of at least 512 tiles of 128 x 256 run the
+   main tile; a 4128 x 4192 output (33 x 17 tiles) has a ragged last tile row
+   (one of four block rows) and tile column (three of eight block columns).
+   K = 256 (two-k-block stages) and K = 288 (odd k-block count: one-k-block
+   stages), all four transposes, random codes and scales: every element of
+   the binary32 and INT8 outputs against the oracle.  Outputs are prefilled
+   (NaN, a code pattern) so an unwritten block cannot pass.
+2. Hidden-4096 GEMMs, every 32nd block row.  The twelve GEMMs of the
+   8192-token block (QKV, out-projection, FC1, FC2; forward, activation
+   gradient, weight gradient) at full size on their workload's data, in the
+   launch configuration the benchmark times: every 32nd output block row
+   (offset per GEMM) against the oracle, binary32 and INT8; the observed
+   difference rates are printed.
+3. Hidden-4096 GEMMs, every element.  Codes in [-2, 2] and power-of-two scales
+   in {1/2, 1, 2}: every partial P, product sigma * P and running sum is then
+   an exact binary32 value (multiples of 1/4 below 2^18), so the output is
+   the exact sum over k-blocks of sigma * P in any order.  The expected value
+   is the float64 product of the dequantized operands (exact for the same
+   reason), and the expected INT8 output is the oracle's per-block
+   requantization of it.  A skipped, duplicated or misplaced tile, a wrong
+   scale index or a stage read before it landed fails here on any block.
+
+The binary32 bar is |gpu - oracle| <= 1e-5 * sum_k |sigma_k P_k| per element
+and 1e-5 normwise; the bound is evaluated on the blocks that differ (none is
+expected: the kernel's arithmetic is the oracle's, so outputs are bit-exact).
+INT8: at most 1 LSB on at most 0.01% of elements, scales within 1e-6.
+"""
+import itertools
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import DEV, assert_f32_close, assert_requant_close, block_abs_terms, dev, host, note
+from int8_block_quantized_amd import inputs
+from int8_block_quantized_amd import jetfire as jf
+
+pytestmark = pytest.mark.gpu
+COMBOS = list(itertools.product((0, 1), (0, 1)))
+
+
+def stored(a, trans):
+    return np.ascontiguousarray(a.T) if trans else a
+
+
+def logical(a, trans):
+    return np.ascontiguousarray(a.T) if trans else a
+
+
+def check_f32(got, ref, A, sA, B, sB, ta, tb, blocks_of_rows, what):
+    """Bit-exact fraction, and the 1e-5 bars on every block that differs.
+    got/ref: the compared rows (2-D); blocks_of_rows maps a row-block index
+    of got to the output block row I."""
+    got = np.asarray(got, np.float32)
+    ref = np.asarray(ref, np.float32)
+    assert not np.isnan(got).any(), f"{what}: unwritten (NaN) outputs"
+    diff = got != ref
+    if diff.any():
+        Al, sAl, Bl, sBl = logical(A, ta), logical(sA, ta), logical(B, tb), logical(sB, tb)
+        rb, cb = np.nonzero(diff.reshape(diff.shape[0] // 32, 32, diff.shape[1] // 32, 32).any(axis=(1, 3)))
+        for r, c in zip(rb, cb):
+            sl = (slice(32 * r, 32 * r + 32), slice(32 * c, 32 * c + 32))
+            assert_f32_close(got[sl], ref[sl], block_abs_terms(Al, sAl, Bl, sBl, blocks_of_rows(r), c),
+                             f"{what} block {blocks_of_rows(r)},{c}")
+        nr = np.linalg.norm(ref.astype(np.float64))
+        assert np.linalg.norm((got - ref).astype(np.float64)) <= 1e-5 * nr, f"{what}: normwise bound"
+    return 1.0 - float(diff.mean())
+
+
+def run_gemm(qa, sa, qb, sb, ta, tb, M, N):
+    """Both output kinds, into prefilled buffers."""
+    c = torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
+    jf.gemm_i8_blockscaled(qa, sa, qb, sb, ta, tb, out="f32", c=c)
+    q = torch.full((M, N), 0x55, dtype=torch.int8, device=DEV)
+    s = torch.full((M // 32, N // 32), float("nan"), dtype=torch.float32, device=DEV)
+    jf.gemm_i8_blockscaled(qa, sa, qb, sb, ta, tb, out="i8", c=q, sc=s)
+    return c, q, s
+
+
+@pytest.mark.parametrize("ta,tb", COMBOS)
+@pytest.mark.parametrize("K", [256, 288])
+def test_main_tile_full_output(ta, tb, K):
+    M, N = 4128, 4192
+    seed = 700 + K // 32 + 2 * ta + tb
+    A = stored(inputs.codes(seed, 0, 0, M, K), ta)
+    B = stored(inputs.codes(seed, 0, 1, K, N), tb)
+    sA = stored(inputs.scales(seed, 0, 2, M // 32, K // 32), ta)
+    sB = stored(inputs.scales(seed, 0, 3, K // 32, N // 32), tb)
+    note(f"main tile full: {M}x{N}x{K} tA={ta} tB={tb}")
+    c, q, s = run_gemm(dev(A), dev(sA), dev(B), dev(sB), ta, tb, M, N)
+    gc, gq, gs = host(c), host(q), host(s)
+    ref = oracle.gemm_f32(A, sA, B, sB, ta=ta, tb=tb)
+    exact = check_f32(gc, ref, A, sA, B, sB, ta, tb, lambda r: r, "main tile f32")
+    # the oracle's INT8 output is the per-block requantization of its binary32 output
+    rq, rs = oracle.requant(ref)
+    frac, srel = assert_requant_close(gq, gs, rq, rs, "main tile i8")
+    note(f"  every element: f32 bit-exact {exact:.6f}, i8 code diffs {frac:.2e}, scale rel {srel:.1e}")
+
+
+_CACHE = {}
+
+
+def quantized(wl, name):
+    key = (wl.wid, name)
+    if key not in _CACHE:
+        if len(_CACHE) > 6:
+            _CACHE.clear()
+        x = wl.make(name)
+        q, s = jf.quantize_block(dev(x))
+        oq, os_ = oracle.quantize(x)
+        np.testing.assert_array_equal(host(q), oq, err_msg=f"{name} codes")
+        np.testing.assert_array_equal(host(s), os_, err_msg=f"{name} scales")
+        _CACHE[key] = (q, s, oq, os_)
+    return _CACHE[key]
+
+
+H4096 = {g[0]: g for g in inputs.hidden4096_block().gemms()}
+
+
+@pytest.mark.parametrize("label", list(H4096))
+def test_hidden4096_every_32nd_block_row(label):
+    wl = inputs.hidden4096_block()
+    _, ta, tb, M, N, K, an, bn = H4096[label]
+    qa, sa, oqa, osa = quantized(wl, an)
+    qb, sb, oqb, osb = quantized(wl, bn)
+    off = zlib.crc32(label.encode()) % 32
+    rows = list(range(off, M // 32, 32))
+    note(f"{label}: M={M} N={N} K={K} tA={ta} tB={tb}, block rows {off}::32 ({len(rows)} rows)")
+    c, q, s = run_gemm(qa, sa, qb, sb, ta, tb, M, N)
+    idx = torch.tensor([32 * I + r for I in rows for r in range(32)], device=DEV)
+    gc = host(c.index_select(0, idx))
+    gq = host(q.index_select(0, idx))
+    gs = host(s.index_select(0, torch.tensor(rows, device=DEV)))
+    del c, q, s
+    blks = [(I, J) for I in rows for J in range(N // 32)]
+    ob = oracle.gemm_f32_blocks(oqa, osa, oqb, osb, blks, ta=ta, tb=tb)      # (nblk, 32, 32)
+    ref = ob.reshape(len(rows), N // 32, 32, 32).transpose(0, 2, 1, 3).reshape(32 * len(rows), N)
+    exact = check_f32(gc, ref, oqa, osa, oqb, osb, ta, tb, lambda r: rows[r], label)
+    rq, rs = oracle.requant(np.ascontiguousarray(ref))
+    frac, srel = assert_requant_close(gq, gs, rq, rs, label)
+    note(f"  {gc.size} elements: f32 bit-exact {exact:.6f}; i8 code diffs {frac:.2e} "
+         f"({int(round(frac * gq.size))} of {gq.size}), scale rel {srel:.1e}")
+
+
+@pytest.mark.parametrize("label", list(H4096))
+def test_hidden4096_every_element_exact(label):
+    _, ta, tb, M, N, K, _, _ = H4096[label]
+    seed = 800 + zlib.crc32(label.encode()) % 1000
+    A = stored(inputs.small_codes(seed, 0, 0, M, K, 2), ta)
+    B = stored(inputs.small_codes(seed, 0, 1, K, N, 2), tb)
+    sA = stored(inputs.pow2_scales(seed, 0, 2, M // 32, K // 32, -1, 1), ta)
+    sB = stored(inputs.pow2_scales(seed, 0, 3, K // 32, N // 32, -1, 1), tb)
+    note(f"{label}: every element, M={M} N={N} K={K} tA={ta} tB={tb}")
+    c, q, s = run_gemm(dev(A), dev(sA), dev(B), dev(sB), ta, tb, M, N)
+    # exact expected value: float64 product of the dequantized operands
+    Ad = torch.from_numpy(oracle.dequantize(A, sA)).to(DEV).double()
+    Bd = torch.from_numpy(oracle.dequantize(B, sB)).to(DEV).double()
+    Ad = Ad.t().contiguous() if ta else Ad
+    Bd = Bd.t().contiguous() if tb else Bd
+    exp = torch.matmul(Ad, Bd)
+    del Ad, Bd
+    assert float(exp.abs().max()) < 2.0 ** 18
+    exp32 = exp.float()
+    assert torch.equal(exp32.double(), exp), "expected value not exact in binary32"
+    del exp
+    bad = (c != exp32)
+    nbad = int(bad.sum())
+    assert not torch.isnan(c).any(), f"{label}: unwritten (NaN) outputs"
+    assert nbad == 0, f"{label}: {nbad} binary32 outputs differ from the exact product"
+    del bad, c
+    rq, rs = oracle.requant(host(exp32))
+    del exp32
+    frac, srel = assert_requant_close(host(q), host(s), rq, rs, label)
+    note(f"  {M * N} elements: f32 exact everywhere; i8 code diffs {frac:.2e}, scale rel {srel:.1e}")
