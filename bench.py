@@ -49,6 +49,12 @@ def parse():
                         "LayerNorm and the hidden-1024 MLP; 0: the step only")
     p.add_argument("--bf16-steps", type=int, default=5,
                    help="steps of the bf16 reference (the same 12 GEMMs with torch.mm in bfloat16; 0 skips it)")
+    p.add_argument("--cpu-full", type=int, default=1,
+                   help="1: also time the oracle on the tiny, GPT2-base, GPT2-medium MLP and memory-bound "
+                        "workloads in full (about 1-2 minutes of CPU); 0: skip")
+    p.add_argument("--ceilings", type=int, default=1,
+                   help="1: measure the ceilings (register-only MFMA and MFMA + rescale loops, streaming "
+                        "copies) the kernels are reported against; 0: skip")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run a plain elementwise copy (dst = src * 1) of MIB mebibytes 5 times (the "
                         "known-size reference for the FETCH_SIZE/WRITE_SIZE counters) and exit")
@@ -192,6 +198,77 @@ def source_digest() -> str:
     return h.hexdigest()[:16]
 
 
+def cpu_info():
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"cpu_model": model, "os_cpu_count": os.cpu_count()}
+
+
+def cpu_full_configs():
+    """The oracle timed in full on the tiny forward, GPT2-base linear,
+    GPT2-medium MLP and memory-bound workloads (every GEMM output block, the
+    whole GELU / GELU backward / quantize) with the threads it uses."""
+    import numpy as np
+
+    import oracle
+    from int8_block_quantized_amd import inputs
+
+    out = {"threads": oracle.get_threads(), **cpu_info()}
+
+    def gemm_set(wl, cache, keep=()):
+        t_all, ops, kept = 0.0, 0, {}
+        for (label, ta, tb, M, N, K, an, bn) in wl.gemms():
+            for n in (an, bn):
+                if n not in cache:
+                    cache[n] = oracle.quantize(wl.make(n))
+            t = time.perf_counter()
+            r = oracle.gemm_i8(*cache[an], *cache[bn], ta=ta, tb=tb)
+            t_all += time.perf_counter() - t
+            ops += 2 * M * N * K
+            if label in keep:
+                kept[label] = r
+        return t_all, ops, kept
+
+    wl = inputs.tiny_forward()
+    t0 = time.perf_counter()
+    qx, sx = oracle.quantize(wl.make("X"))
+    qw, sw = oracle.quantize(wl.make("W"))
+    oracle.gemm_i8(qx, sx, qw, sw)
+    out["tiny_forward"] = {"seconds": round(time.perf_counter() - t0, 4),
+                           "what": "quantize X and W (256x256), block-scaled GEMM 256^3 with INT8 output"}
+    for key, wl in (("gpt2_base_linear", inputs.gpt2_base_linear()), ("gpt2_medium_mlp", inputs.gpt2_medium_mlp())):
+        cache = {}
+        secs, ops, kept = gemm_set(wl, cache, keep=("fc1.fwd",))
+        e = {"gemm_seconds": round(secs, 2), "gemm_ops": ops, "tops": round(ops / secs / 1e12, 5)}
+        if key == "gpt2_medium_mlp":
+            t = time.perf_counter()
+            oracle.gelu(*kept["fc1.fwd"])
+            e["gelu_seconds"] = round(time.perf_counter() - t, 2)
+            e["gelu_what"] = "INT8 GELU of FC1's forward output, 8192x4096"
+        e["what"] = f"{wl.name}: every GEMM (fwd, dgrad, wgrad) in full, INT8 output"
+        out[key] = e
+        log(f"cpu full: {key} {e}")
+    x = inputs.memory_bound().make("X")
+    t = time.perf_counter()
+    q, sc = oracle.quantize(x)
+    tq = time.perf_counter() - t
+    t = time.perf_counter()
+    oracle.gelu(q, sc)
+    tg = time.perf_counter() - t
+    n = x.size
+    out["memory_bound"] = {"quantize_seconds": round(tq, 2), "quantize_gbs": round(n * (5 + 4 / 1024) / tq / 1e9, 2),
+                           "gelu_seconds": round(tg, 2), "gelu_gbs": round(n * (2 + 8 / 1024) / tg / 1e9, 2),
+                           "what": "16384x16384: quantize fp32 -> INT8, then INT8 GELU, in full"}
+    out["kind"] = "oracle"
+    return out
+
+
 def cpu_baseline(step, target_s):
     """The oracle, as it stands, on a bounded sample of the same workload."""
     import numpy as np
@@ -236,7 +313,8 @@ def cpu_baseline(step, target_s):
     frac = 2e-4 * max(1.0, target_s / max(s0, 1e-3))
     frac = min(frac, 0.05)
     ops, secs = sample(frac, seed=2)
-    return {"value": ops / secs / 1e12, "unit": "TOPS", "cores": threads, "kind": "oracle",
+    return {"value": ops / secs / 1e12, "unit": "TOPS", "cores": threads, "kind": "oracle", **cpu_info(),
+            "extrapolated": True,
             "sample": (f"{frac * 100:.3f}% of the output 32x32 blocks of each of the 12 GEMMs "
                        f"(random, seeded), INT8 output, {ops / 1e9:.1f} G ops in {secs:.1f} s; "
                        "synthetic H/dH stand in for the GELU output and the GELU-backward output")}
@@ -465,6 +543,97 @@ def mlp1024_section(reps=10):
                     "6 INT8 GEMMs vs the same 6 GEMM shapes as torch.mm in bfloat16"}
 
 
+CEIL = {"mfma_only": 0, "mfma_rescale": 1, "mfma_bias_rescale": 2, "copy_i8": 3, "copy_f32_to_i8": 4,
+        "copy_2i8_to_i8": 5}
+
+
+def ceilings_section():
+    """Measured ceilings (libjfceil.so): the INT8 matrix-core rate with no
+    other work, the GEMM's per-(block, k-block) arithmetic (MFMA, convert,
+    fma) with no memory traffic, the same with the partial converted through
+    the MFMA's C operand, and streaming copies with the memory-bound kernels'
+    byte patterns on 16384^2 elements (two input sets in turn)."""
+    import ctypes
+
+    from int8_block_quantized_amd import _build
+
+    if not os.path.exists(_build.CEIL_PATH):
+        _build.build_ceilings()
+    lib = ctypes.CDLL(_build.CEIL_PATH)
+    lib.jfc_measure.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.POINTER(ctypes.c_double),
+                                ctypes.POINTER(ctypes.c_double)]
+    lib.jfc_measure.restype = ctypes.c_int
+    n = 16384 * 16384
+    plan = {"mfma_only": (20000, 10), "mfma_rescale": (5000, 10), "mfma_bias_rescale": (5000, 10),
+            "copy_i8": (n, 20), "copy_f32_to_i8": (4 * n, 10), "copy_2i8_to_i8": (n, 20)}
+    out = {}
+    for name, (size, reps) in plan.items():
+        rate, us = ctypes.c_double(), ctypes.c_double()
+        rc = lib.jfc_measure(CEIL[name], size, reps, ctypes.byref(rate), ctypes.byref(us))
+        if rc != 0:
+            raise RuntimeError(f"jfc_measure({name}) failed: hip error {rc}")
+        unit = "TOPS" if name.startswith("mfma") else "GB/s"
+        out[name] = {"rate": round(rate.value, 1), "unit": unit, "us": round(us.value, 1)}
+    out["what"] = ("register-only loops on 256 CUs x 4 wavefronts per SIMD (2x2 output blocks per wavefront): "
+                   "v_mfma_i32_32x32x32_i8 alone; each MFMA followed by the GEMM's rescale (cvt + fma per "
+                   "result); the same with the bias conversion (sub + fma); streaming copies 16384^2 "
+                   "int8->int8, fp32->int8, two int8 -> int8")
+    return out
+
+
+def small_configs_section(reps=50):
+    """GPU times of the tiny forward (256^3) and the GPT2-base linear
+    (4096 tokens, 768 -> 3072) workloads."""
+    import torch
+
+    from int8_block_quantized_amd import inputs
+    from int8_block_quantized_amd import jetfire as jf
+
+    dev = torch.device("cuda:0")
+    out = {}
+    wl = inputs.tiny_forward()
+    x, w = (torch.from_numpy(wl.make(n)).to(dev) for n in ("X", "W"))
+    qx, sx = jf.quantize_block(x)
+    qw, sw = jf.quantize_block(w)
+    qy, sy = jf.gemm_i8_blockscaled(qx, sx, qw, sw)
+    cy = jf.gemm_i8_blockscaled(qx, sx, qw, sw, out="f32")
+
+    def tiny_i8():
+        jf.quantize_block(x, q=qx, s=sx)
+        jf.quantize_block(w, q=qw, s=sw)
+        jf.gemm_i8_blockscaled(qx, sx, qw, sw, c=qy, sc=sy)
+
+    def tiny_f32():
+        jf.quantize_block(x, q=qx, s=sx)
+        jf.quantize_block(w, q=qw, s=sw)
+        jf.gemm_i8_blockscaled(qx, sx, qw, sw, out="f32", c=cy)
+        jf.requant_block(cy, q=qy, s=sy)
+
+    ops = 2 * 256 ** 3
+    for key, fn in (("tiny_i8_out_us", tiny_i8), ("tiny_f32_out_requant_us", tiny_f32)):
+        out[key] = round(_time_us(fn, reps), 2)
+    out["tiny_gemm_i8_us"] = round(_time_us(lambda: jf.gemm_i8_blockscaled(qx, sx, qw, sw, c=qy, sc=sy), reps), 2)
+    out["tiny_gemm_tops"] = round(ops / (out["tiny_gemm_i8_us"] * 1e-6) / 1e12, 2)
+    out["tiny_what"] = ("tiny forward 256x256x256: quantize X and W, GEMM with INT8 output (i8_out); or binary32 "
+                        "output then jf_requant_block (f32_out_requant); the GEMM alone (gemm_i8)")
+    wl = inputs.gpt2_base_linear()
+    fp = {n: torch.from_numpy(wl.make(n)).to(dev) for n in ("X", "W", "dY")}
+    q = {n: jf.quantize_block(t) for n, t in fp.items()}
+    res = {}
+    tot_us, tot_ops = 0.0, 0
+    for (label, ta, tb, M, N, K, an, bn) in wl.gemms():
+        c, sc = jf.gemm_i8_blockscaled(q[an][0], q[an][1], q[bn][0], q[bn][1], ta, tb)
+        us = _time_us(lambda: jf.gemm_i8_blockscaled(q[an][0], q[an][1], q[bn][0], q[bn][1], ta, tb, c=c, sc=sc),
+                      reps)
+        res[label] = {"us": round(us, 1), "tops": round(2 * M * N * K / (us * 1e-6) / 1e12, 1)}
+        tot_us += us
+        tot_ops += 2 * M * N * K
+    out["gpt2_base_linear"] = {**res, "total_us": round(tot_us, 1), "tops": round(tot_ops / (tot_us * 1e-6) / 1e12, 1),
+                               "what": "4096 tokens, 768 -> 3072: fwd, dgrad, wgrad with INT8 output"}
+    torch.cuda.empty_cache()
+    return out
+
+
 def memory_bound_section(reps=20):
     """The memory-bound workload: a 16384 x 16384 fp32 activation (N(0,1),
     1% of columns x100) through jf_quantize_block, then jf_gelu_i8 on its codes.
@@ -559,11 +728,15 @@ def main():
     wall = time.perf_counter() - wall0
     ms_step = t_start.elapsed_time(t_end) / args.steps
 
-    # per-kernel durations (ms), averaged over the timed steps
-    per = {}
+    # per-kernel durations (ms) over the timed steps: the mean (what the
+    # rocprofv3 kernel statistics average, used for the roofline) and the median
+    per, per_med = {}, {}
     for i, (kind, label, a) in enumerate(step.ops):
-        d = [ev[k][i][0].elapsed_time(ev[k][i][1]) for k in range(args.steps)]
+        d = sorted(ev[k][i][0].elapsed_time(ev[k][i][1]) for k in range(args.steps))
         per[label] = sum(d) / len(d)
+        per_med[label] = d[len(d) // 2]
+    step_spans = sorted(ev[k][0][0].elapsed_time(ev[k][n_ops - 1][1]) for k in range(args.steps))
+    ms_step_median = step_spans[len(step_spans) // 2]
 
     families = {}
     for label, m in step.meta.items():
@@ -575,7 +748,7 @@ def main():
     dom_name, dom = max(families.items(), key=lambda kv: kv[1]["ms"])
     if "gemm" in dom_name:
         achieved = dom["ops"] / (dom["ms"] * 1e-3) / 1e12
-        roof = {"bound": "mfma", "unit": "TFLOP/s", "peak": INT8_PEAK_TOPS}
+        roof = {"bound": "mfma", "unit": "TOPS", "peak": INT8_PEAK_TOPS}
     else:
         achieved = dom["bytes"] / (dom["ms"] * 1e-3) / 1e9
         roof = {"bound": "hbm", "unit": "GB/s", "peak": HBM_PEAK_GBS}
@@ -591,11 +764,11 @@ def main():
     value = step.gemm_ops / (ms_step * 1e-3) / 1e12
     kernels = {}
     for label, m in step.meta.items():
-        e = {"us": round(per[label] * 1e3, 1)}
+        e = {"us_median": round(per_med[label] * 1e3, 1), "us_mean": round(per[label] * 1e3, 1)}
         if m["kind"] == "gemm":
-            e["tops"] = round(m["ops"] / (per[label] * 1e-3) / 1e12, 1)
+            e["tops"] = round(m["ops"] / (per_med[label] * 1e-3) / 1e12, 1)
         else:
-            e["gbs"] = round(m["bytes"] / (per[label] * 1e-3) / 1e9, 1)
+            e["gbs"] = round(m["bytes"] / (per_med[label] * 1e-3) / 1e9, 1)
         kernels[label] = e
 
     bf16 = None
@@ -623,6 +796,29 @@ def main():
 
     mlp1024 = mlp1024_section() if args.extras else None
     membound = memory_bound_section() if args.extras else None
+    small = small_configs_section() if args.extras else None
+    ceil = None
+    if args.ceilings:
+        try:
+            ceil = ceilings_section()
+        except Exception as exc:  # context only, never gating
+            log(f"ceilings failed: {exc!r}")
+    if ceil:
+        if roof["bound"] == "mfma":
+            roof["ceiling"] = ceil["mfma_rescale"]["rate"]
+            roof["ceiling_what"] = "measured register-only MFMA + rescale (cvt + fma) loop: this numerics' bound"
+            roof["frac_of_ceiling"] = round(roof["achieved"] / ceil["mfma_rescale"]["rate"], 4)
+            roof["mfma_only_measured"] = ceil["mfma_only"]["rate"]
+        if membound:
+            for name, cp in (("quantize", "copy_f32_to_i8"), ("gelu", "copy_i8")):
+                membound[name]["copy_bound_gbs"] = ceil[cp]["rate"]
+                membound[name]["frac_of_copy"] = round(membound[name]["gbs"] / ceil[cp]["rate"], 4)
+    cpu_full = None
+    if args.cpu_full:
+        try:
+            cpu_full = cpu_full_configs()
+        except Exception as exc:  # reported, never gating
+            log(f"cpu full configs failed: {exc!r}")
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -639,6 +835,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        "ms_per_step_median": round(ms_step_median, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -653,6 +850,9 @@ def main():
         "gemm_only_tops": round(step.gemm_ops / (gemm_ms * 1e-3) / 1e12, 2),
         "roofline": roof,
         "cpu_baseline": cpu,
+        "cpu_full_configs": cpu_full,
+        "ceilings": ceil,
+        "small_configs": small,
         "bf16_reference": bf16,
         "int8_library_reference": i8lib,
         "quant_error": qerr,

@@ -62,6 +62,24 @@ PER_SOURCE_FLAGS = {
 }
 
 
+CEIL_SRC = os.path.join(PKG, "ceilings", "ceilings.hip")
+CEIL_PATH = os.path.join(PKG, "libjfceil.so")
+
+
+def build_ceilings(verbose: bool = False) -> str:
+    """Compile the benchmark's measured-ceiling kernels (register-only MFMA
+    loops, streaming copies) into libjfceil.so.  Not part of the hot path."""
+    tmp = CEIL_PATH + ".tmp"
+    cmd = ["hipcc", *HIPCC_FLAGS, CEIL_SRC, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed:\n{res.stdout}\n{res.stderr}")
+    os.replace(tmp, CEIL_PATH)
+    return CEIL_PATH
+
+
 def build(verbose: bool = False) -> str:
     """Compile every HIP source into libjetfire.so (always recompiles): one
     object per source (in parallel), then one shared-library link."""

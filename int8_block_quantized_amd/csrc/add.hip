@@ -32,8 +32,8 @@ __global__ __launch_bounds__(256) void k_add_i8(const int8_t *__restrict__ qa, i
         const int8_t *pb = qb + (gi * kBlock + r8) * ldb + (int64_t)bj * kBlock + colb;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            wa[i] = *reinterpret_cast<const u32x4 *>(pa + 8 * i * lda);
-            wb[i] = *reinterpret_cast<const u32x4 *>(pb + 8 * i * ldb);
+            wa[i] = ld_stream(reinterpret_cast<const u32x4 *>(pa + 8 * i * lda));
+            wb[i] = ld_stream(reinterpret_cast<const u32x4 *>(pb + 8 * i * ldb));
         }
     }
     const float sa_l = sa[gi * nbc + bj], sb_l = sb[gi * nbc + bj];

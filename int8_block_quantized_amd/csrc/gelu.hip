@@ -163,7 +163,7 @@ __global__ __launch_bounds__(256) void k_gelu_i8(const int8_t *__restrict__ q, i
         const int bj = min((int)(grp - gi * ngc) * kGroup + b, nbc - 1);
         const int8_t *src = q + (gi * kBlock + r8) * ldq + (int64_t)bj * kBlock + colb;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) w[p][i] = *reinterpret_cast<const u32x4 *>(src + 8 * i * ldq);
+        for (int i = 0; i < 4; ++i) w[p][i] = ld_stream(reinterpret_cast<const u32x4 *>(src + 8 * i * ldq));
         scl[p] = s[gi * nbc + bj];
     }
 
@@ -271,7 +271,7 @@ __global__ __launch_bounds__(256) void k_gelu_i8(const int8_t *__restrict__ q, i
                     od[d] = __builtin_amdgcn_perm(__builtin_amdgcn_perm(r[3], r[2], 0x0c0c0400u),
                                                   __builtin_amdgcn_perm(r[1], r[0], 0x0c0c0400u), 0x05040100u);
                 }
-                *reinterpret_cast<u32x4 *>(dst + 8 * i * ldqo) = u32x4{od[0], od[1], od[2], od[3]};
+                st_stream(reinterpret_cast<u32x4 *>(dst + 8 * i * ldqo), u32x4{od[0], od[1], od[2], od[3]});
             }
         }
     }

@@ -59,8 +59,8 @@ __global__ __launch_bounds__(256) void k_gelu_bwd_i8(const int8_t *__restrict__ 
         const int8_t *px = qx + (gi * kBlock + r8) * ldx + (int64_t)bj * kBlock + colb;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            wy[i] = *reinterpret_cast<const u32x4 *>(py + 8 * i * lddy);
-            wx[i] = *reinterpret_cast<const u32x4 *>(px + 8 * i * ldx);
+            wy[i] = ld_stream(reinterpret_cast<const u32x4 *>(py + 8 * i * lddy));
+            wx[i] = ld_stream(reinterpret_cast<const u32x4 *>(px + 8 * i * ldx));
         }
     }
     const float sdy_l = sdy[gi * nbc + bj], sx_l = sx[gi * nbc + bj];

@@ -20,6 +20,22 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// Streaming HBM access of the memory-bound kernels: every input and output
+// element is touched once, so loads and stores carry the nontemporal hint.
+#ifndef JF_NT
+#define JF_NT 1
+#endif
+template <typename T>
+__device__ __forceinline__ T ld_stream(const T *p) {
+    if constexpr (JF_NT) return __builtin_nontemporal_load(p);
+    else return *p;
+}
+template <typename T>
+__device__ __forceinline__ void st_stream(T *p, T v) {
+    if constexpr (JF_NT) __builtin_nontemporal_store(v, p);
+    else *p = v;
+}
+
 // Lane exchange inside rows of 16 lanes (DPP); all lanes valid.
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp(uint32_t v) {

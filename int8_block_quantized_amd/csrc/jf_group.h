@@ -43,9 +43,9 @@ __device__ __forceinline__ void store_group_codes(const float (&y)[64], float sc
 #pragma unroll
             for (int e = 0; e < 16; ++e) code[e] = 0;
         }
-        *reinterpret_cast<u32x4 *>(dst + 8 * i * ld) =
-            u32x4{pack4(code[0], code[1], code[2], code[3]), pack4(code[4], code[5], code[6], code[7]),
-                  pack4(code[8], code[9], code[10], code[11]), pack4(code[12], code[13], code[14], code[15])};
+        st_stream(reinterpret_cast<u32x4 *>(dst + 8 * i * ld),
+                  u32x4{pack4(code[0], code[1], code[2], code[3]), pack4(code[4], code[5], code[6], code[7]),
+                        pack4(code[8], code[9], code[10], code[11]), pack4(code[12], code[13], code[14], code[15])});
     }
 }
 

@@ -41,11 +41,11 @@ template <>
 struct Seg<float> {
     static constexpr int kElems = 4;              // elements per lane and row (16 bytes)
     static __device__ __forceinline__ void load(const float *p, float *v) {
-        const f32x4 f = *reinterpret_cast<const f32x4 *>(p);
+        const f32x4 f = ld_stream(reinterpret_cast<const f32x4 *>(p));
         v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
     }
     static __device__ __forceinline__ void store(int8_t *p, const int *c) {
-        *reinterpret_cast<uint32_t *>(p) = pack4(c[0], c[1], c[2], c[3]);
+        st_stream(reinterpret_cast<uint32_t *>(p), pack4(c[0], c[1], c[2], c[3]));
     }
 };
 
@@ -54,7 +54,7 @@ struct Seg<uint16_t> {
     static constexpr int kElems = 8;
     // bfloat16 -> binary32 is exact: the 16 bits become the high half.
     static __device__ __forceinline__ void load(const uint16_t *p, float *v) {
-        const u32x4 w = *reinterpret_cast<const u32x4 *>(p);
+        const u32x4 w = ld_stream(reinterpret_cast<const u32x4 *>(p));
         const uint32_t d[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -63,7 +63,7 @@ struct Seg<uint16_t> {
         }
     }
     static __device__ __forceinline__ void store(int8_t *p, const int *c) {
-        *reinterpret_cast<u32x2 *>(p) = u32x2{pack4(c[0], c[1], c[2], c[3]), pack4(c[4], c[5], c[6], c[7])};
+        st_stream(reinterpret_cast<u32x2 *>(p), u32x2{pack4(c[0], c[1], c[2], c[3]), pack4(c[4], c[5], c[6], c[7])});
     }
 };
 
