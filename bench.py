@@ -465,7 +465,8 @@ def data_flow_ops_section(step, reps=20):
                              "bytes_per_element": 3.0117},
             "layernorm": {"us": round(ln_us, 1), "gbs": round((2 * n + 8 * nblk) / (ln_us * 1e-6) / 1e9, 1),
                           "bytes_per_element": 2.0078},
-            "what": "R = X + A and LayerNorm(R) on 8192x4096 per-block INT8 tensors (INT8 in and out)"}
+            "what": "R = X + A and LayerNorm(R) on 8192x4096 per-block INT8 tensors (INT8 in and out); GB/s of "
+                    "algorithmic bytes (inputs and outputs once)"}
 
 
 def mlp1024_section(reps=10):

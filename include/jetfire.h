@@ -45,7 +45,11 @@
  *        JF_ERR_ALIAS  an output overlaps an input or another output
  *        JF_ERR_HIP    the kernel launch failed (hipGetLastError)
  *    A size of zero is valid: nothing is launched for an empty output, and a
- *    GEMM with K = 0 writes zeros (binary32) or zero codes and scales.
+ *    GEMM with K = 0 writes zeros (binary32) or zero codes and scales.  (This
+ *    departs on purpose from treating an empty size as a shape error: torch
+ *    hands out empty tensors, and an empty output or a K = 0 contraction has
+ *    a well-defined result.  JF_ERR_ARG, for flags and granularities out of
+ *    range, is likewise an addition to the shape and pointer codes.)
  *  - Inputs must be finite; NaN or Inf inputs give unspecified outputs.
  *  - Entry points keep no state and are safe to call from several threads.
  */

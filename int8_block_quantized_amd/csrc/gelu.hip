@@ -43,7 +43,7 @@
 namespace jf {
 namespace {
 
-// The binary64 reference value (gelu_tail: the normal-tail expansion, 66
+// The binary64 reference value (gelu_tail: the normal-tail expansion, 67
 // VALU instructions against 144 for the library erfc) as a call: one copy of
 // the code instead of one per use, and its registers stay out of the
 // kernel's loop.

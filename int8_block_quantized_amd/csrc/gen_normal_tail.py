@@ -1,7 +1,11 @@
 """Writes jf_normal_tail.h: the binary64 upper normal tail
 Q(z) = erfc(z/sqrt 2)/2 used by the INT8 GELU backward kernel's derivative
 tables (GELU'(x) = Phi(x) + x phi(x), the derivative of the erf form x Phi(x)
-of the Jetfire summary's INT8 data flow, "Approach"; Phi(-z) = Q(z)).
+of the Jetfire summary's INT8 data flow, "Approach"; Phi(-z) = Q(z)) and by
+the INT8 GELU forward kernel's binary64 reference (block maxima and rare
+fallbacks), which also takes exp(-u) from this header (Cody-Waite reduction
+by a two-part ln 2, degree-13 Taylor polynomial, within 1.2e-16 relative on
+[0, 700]).
 
 Q is written as Q(z) = M(z) exp(-z^2/2) with M(z) = Q(z) exp(z^2/2), a
 smooth function that decays like 1/(z sqrt(2 pi)).  M is approximated by a
@@ -81,10 +85,15 @@ def main():
     err = max_rel_error(a)
     out = sys.stdout
     out.write("// jf_normal_tail.h -- the upper normal tail Q(z) = erfc(z/sqrt 2)/2 in\n")
-    out.write("// binary64 for the INT8 GELU backward.  Written by gen_normal_tail.py\n")
-    out.write("// (Chebyshev interpolant of the scaled tail M(z) = Q(z) exp(z^2/2) in\n")
-    out.write(f"// t = (z - {K})/(z + {K}), degree {N}; largest relative error of M's binary64\n")
-    out.write(f"// evaluation on [0, 40]: {err:.2e}).  Do not edit by hand.\n")
+    out.write("// binary64, used by the INT8 GELU backward (its GELU' tables) and by the\n")
+    out.write("// INT8 GELU forward (its binary64 reference for block maxima and rare\n")
+    out.write("// fallbacks).  Written by gen_normal_tail.py: the Chebyshev interpolant of\n")
+    out.write("// the scaled tail M(z) = Q(z) exp(z^2/2) in t = (z - 4)/(z + 4), degree\n")
+    out.write(f"// {N} (largest relative error of M's binary64 evaluation on [0, 40]:\n")
+    out.write(f"// {err:.2e}); for the forward GELU also exp(-u) by a Cody-Waite reduction\n")
+    out.write("// with a two-part ln 2 and a degree-13 Taylor polynomial (within 1.2e-16\n")
+    out.write("// relative on [0, 700]) and sreg(), which keeps binary64 constants in\n")
+    out.write("// scalar registers.  Do not edit by hand.\n")
     out.write("#pragma once\n\n#include <hip/hip_runtime.h>\n\nnamespace jf {\n\n")
     out.write(f"constexpr double kTailK = {K}.0;\n")
     out.write(f"constexpr int kTailDegree = {N};\n")

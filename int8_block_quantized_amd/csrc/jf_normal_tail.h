@@ -1,8 +1,13 @@
 // jf_normal_tail.h -- the upper normal tail Q(z) = erfc(z/sqrt 2)/2 in
-// binary64 for the INT8 GELU backward.  Written by gen_normal_tail.py
-// (Chebyshev interpolant of the scaled tail M(z) = Q(z) exp(z^2/2) in
-// t = (z - 4)/(z + 4), degree 24; largest relative error of M's binary64
-// evaluation on [0, 40]: 4.50e-16).  Do not edit by hand.
+// binary64, used by the INT8 GELU backward (its GELU' tables) and by the
+// INT8 GELU forward (its binary64 reference for block maxima and rare
+// fallbacks).  Written by gen_normal_tail.py: the Chebyshev interpolant of
+// the scaled tail M(z) = Q(z) exp(z^2/2) in t = (z - 4)/(z + 4), degree
+// 24 (largest relative error of M's binary64 evaluation on [0, 40]:
+// 4.50e-16); for the forward GELU also exp(-u) by a Cody-Waite reduction
+// with a two-part ln 2 and a degree-13 Taylor polynomial (within 1.2e-16
+// relative on [0, 700]) and sreg(), which keeps binary64 constants in
+// scalar registers.  Do not edit by hand.
 #pragma once
 
 #include <hip/hip_runtime.h>

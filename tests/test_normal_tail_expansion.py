@@ -1,5 +1,7 @@
 """CPU check of the coefficients in jf_normal_tail.h (the binary64 expansion of
-the upper normal tail that the INT8 GELU backward kernel uses for GELU').
+the upper normal tail that the INT8 GELU backward kernel uses for GELU' and the
+INT8 GELU forward kernel uses for its binary64 reference, with the header's
+exp(-u)).
 
 M(z) = Q(z) exp(z^2/2), Q the upper normal tail, is evaluated from the
 header's power-basis coefficients in t = (z - K)/(z + K) with binary64
