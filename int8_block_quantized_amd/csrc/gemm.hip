@@ -106,6 +106,29 @@
 #ifndef JF_GEMM_WAVES_PER_EU
 #define JF_GEMM_WAVES_PER_EU 4
 #endif
+// Larger tile for the gradient GEMMs' grids that have at least
+// JF_GEMM_BIG_MIN tiles of it and at least JF_GEMM_BIG_WORK (tiles x
+// k-blocks) of work: 4 x 4 wavefronts of the same 2 x 2 blocks (a 256 x 256
+// tile, one workgroup of sixteen wavefronts per CU).  Each MFMA then needs a
+// third fewer operand bytes from L2 (256 against 384), and at the power the
+// GEMMs draw the GPU's clock rises with less memory traffic (about 2.14
+// against 2.05 GHz), which on the activation- and weight-gradient layouts
+// outweighs the sixteen-wavefront barrier (+2 to +9% on the hidden-4096
+// shapes); on the forward layout (B row-contiguous), on grids of fewer tiles
+// and on short contractions (8192 x 4096 x 4096: one workgroup per CU for
+// only two tiles' worth of k-blocks) it was 1-5% slower.
+#ifndef JF_GEMM_BIG_GM
+#define JF_GEMM_BIG_GM 4
+#endif
+#ifndef JF_GEMM_BIG_GN
+#define JF_GEMM_BIG_GN 4
+#endif
+#ifndef JF_GEMM_BIG_MIN
+#define JF_GEMM_BIG_MIN 512
+#endif
+#ifndef JF_GEMM_BIG_WORK
+#define JF_GEMM_BIG_WORK (1 << 17)
+#endif
 
 #define JF_GEMM_OCCUPANCY __attribute__((amdgpu_waves_per_eu(JF_GEMM_WAVES_PER_EU)))
 
@@ -633,11 +656,20 @@ hipError_t dispatch_kb(int64_t M, int64_t N, int64_t K, const int8_t *A, int64_t
     // 32-byte ones load much worse when an operand is k-contiguous) in a
     // two-deep ring, which leaves LDS for four wavefronts per SIMD.  A stage
     // must lie inside K; odd K/32 falls back to one k-block per stage.
-    // Grids of fewer than JF_GEMM_SMALL_BELOW main tiles take the smaller tile
-    // (the per-element k order, and so every result bit, is the same).
+    // Tile: the 256 x 256 one for the gradient layouts when the grid has at
+    // least JF_GEMM_BIG_MIN of them, else the 128 x 256 main tile; grids of fewer than
+    // JF_GEMM_SMALL_BELOW main tiles take the smaller tile (the per-element
+    // k order, and so every result bit, is the same for all three).
     if ((K / kBlock) % JF_GEMM_KB != 0)
         return dispatch_narrow<JF_GEMM_WM, JF_GEMM_WN, 2, 2, 1, 4, A_KC, B_KC, OUT_I8>(M, N, K, A, lda, sA, B, ldb,
                                                                                  sB, C, ldc, sC, stream);
+    constexpr int64_t GBM = JF_GEMM_BIG_GM * JF_GEMM_WM * kBlock, GBN = JF_GEMM_BIG_GN * JF_GEMM_WN * kBlock;
+    if constexpr (!(A_KC && !B_KC)) {   // not the forward layout
+        const int64_t big = ((M + GBM - 1) / GBM) * ((N + GBN - 1) / GBN);
+        if (JF_GEMM_BIG_MIN > 0 && big >= JF_GEMM_BIG_MIN && big * (K / kBlock) >= JF_GEMM_BIG_WORK)
+            return dispatch_narrow<JF_GEMM_WM, JF_GEMM_WN, JF_GEMM_BIG_GM, JF_GEMM_BIG_GN, JF_GEMM_KB, JF_GEMM_S,
+                                   A_KC, B_KC, OUT_I8>(M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC, stream);
+    }
     constexpr int64_t BM = JF_GEMM_GM * JF_GEMM_WM * kBlock, BN = JF_GEMM_GN * JF_GEMM_WN * kBlock;
     const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
     if (tiles < JF_GEMM_SMALL_BELOW)

@@ -21,6 +21,9 @@
    reason), and the expected INT8 output is the oracle's per-block
    requantization of it.  A skipped, duplicated or misplaced tile, a wrong
    scale index or a stage read before it landed fails here on any block.
+4. The 256 x 256 tile of the gradient layouts on a ragged 8224 x 4192 grid:
+   every element with the exact construction, the edge blocks against the
+   oracle with real codes and scales.
 
 The binary32 bar is |gpu - oracle| <= 1e-5 * sum_k |sigma_k P_k| per element
 and 1e-5 normwise; the bound is evaluated on the blocks that differ (none is
@@ -176,3 +179,48 @@ def test_hidden4096_every_element_exact(label):
     del exp32
     frac, srel = assert_requant_close(host(q), host(s), rq, rs, label)
     note(f"  {M * N} elements: f32 exact everywhere; i8 code diffs {frac:.2e}, scale rel {srel:.1e}")
+
+
+@pytest.mark.parametrize("ta,tb", [(0, 1), (1, 0), (1, 1)])
+def test_big_tile_ragged_every_element(ta, tb):
+    """The 256 x 256 tile (gradient layouts, grids of >= 512 such tiles with
+    enough k-blocks) on an 8224 x 4192 output: 33 x 17 tiles with a ragged
+    last tile row (one block row of eight) and column (three block columns of
+    eight), K = 8192.  Every element with the exact small-code construction,
+    and the edge blocks against the oracle with real codes and scales."""
+    M, N, K = 8224, 4192, 8192
+    seed = 900 + 2 * ta + tb
+    A = stored(inputs.small_codes(seed, 0, 0, M, K, 2), ta)
+    B = stored(inputs.small_codes(seed, 0, 1, K, N, 2), tb)
+    sA = stored(inputs.pow2_scales(seed, 0, 2, M // 32, K // 32, -1, 1), ta)
+    sB = stored(inputs.pow2_scales(seed, 0, 3, K // 32, N // 32, -1, 1), tb)
+    note(f"big tile ragged: {M}x{N}x{K} tA={ta} tB={tb}, every element")
+    c, q, s = run_gemm(dev(A), dev(sA), dev(B), dev(sB), ta, tb, M, N)
+    Ad = torch.from_numpy(oracle.dequantize(A, sA)).to(DEV).double()
+    Bd = torch.from_numpy(oracle.dequantize(B, sB)).to(DEV).double()
+    exp = torch.matmul(Ad.t().contiguous() if ta else Ad, Bd.t().contiguous() if tb else Bd)
+    del Ad, Bd
+    exp32 = exp.float()
+    assert torch.equal(exp32.double(), exp)
+    assert not torch.isnan(c).any()
+    nbad = int((c != exp32).sum())
+    assert nbad == 0, f"{nbad} binary32 outputs differ from the exact product"
+    rq, rs = oracle.requant(host(exp32))
+    frac, srel = assert_requant_close(host(q), host(s), rq, rs, "big tile ragged (exact)")
+    del c, q, s, exp, exp32
+    # real codes and scales on the ragged edge blocks
+    A = stored(inputs.codes(seed, 1, 0, M, K), ta)
+    B = stored(inputs.codes(seed, 1, 1, K, N), tb)
+    sA = stored(inputs.scales(seed, 1, 2, M // 32, K // 32), ta)
+    sB = stored(inputs.scales(seed, 1, 3, K // 32, N // 32), tb)
+    c, q, s = run_gemm(dev(A), dev(sA), dev(B), dev(sB), ta, tb, M, N)
+    nbM, nbN = M // 32, N // 32
+    blks = sorted({(nbM - 1, J) for J in range(nbN)} | {(I, J) for I in range(0, nbM, 16) for J in range(nbN - 3, nbN)})
+    gc, gq, gs = host(c), host(q), host(s)
+    oc = oracle.gemm_f32_blocks(A, sA, B, sB, blks, ta=ta, tb=tb)
+    np.testing.assert_array_equal(np.stack([gc[32 * I:32 * I + 32, 32 * J:32 * J + 32] for I, J in blks]), oc)
+    oq, os_ = oracle.gemm_i8_blocks(A, sA, B, sB, blks, ta=ta, tb=tb)
+    frac2, srel2 = assert_requant_close(np.stack([gq[32 * I:32 * I + 32, 32 * J:32 * J + 32] for I, J in blks]),
+                                        np.array([gs[I, J] for I, J in blks]), oq, os_, "big tile ragged edges")
+    note(f"  exact: f32 exact everywhere, i8 code diffs {frac:.2e}; {len(blks)} edge blocks with real scales: "
+         f"f32 bit-exact, i8 code diffs {frac2:.2e}")
