@@ -193,7 +193,7 @@ def read_traffic():
 
 def source_digest() -> str:
     h = hashlib.sha256()
-    for f in ("csrc/gemm.hip", "csrc/jf_device.h", "_build.py"):   # the kernel and how it is compiled
+    for f in ("csrc/gemm.hip", "csrc/jf_tile_order.h", "csrc/jf_device.h", "_build.py"):   # the kernel, how it is compiled
         h.update(open(os.path.join(ROOT, "int8_block_quantized_amd", f), "rb").read())
     return h.hexdigest()[:16]
 
