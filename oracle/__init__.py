@@ -60,6 +60,8 @@ def _load():
         lib.jfo_quantize_bf16.argtypes = [ptr, i64, i64, ptr, ptr]
         lib.jfo_requant.argtypes = [ptr, i64, i64, ptr, ptr]
         lib.jfo_dequantize.argtypes = [ptr, ptr, i64, i64, ptr]
+        lib.jfo_dequantize_bf16.argtypes = [ptr, ptr, i64, i64, ptr]
+        lib.jfo_bf16_round.argtypes = [ptr, i64, ptr]
         lib.jfo_gemm_f32.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64, ptr, ptr, ptr, ptr, ptr]
         lib.jfo_gemm_f32_blocks.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64,
                                             ptr, ptr, ptr, ptr, ptr, i64, ptr]
@@ -142,6 +144,25 @@ def dequantize(q: np.ndarray, s: np.ndarray) -> np.ndarray:
     R, C = q.shape
     out = np.empty((R, C), np.float32)
     _chk(_load().jfo_dequantize(_p(q), _p(s), R, C, _p(out)), "dequantize")
+    return out
+
+
+def dequantize_bf16(q: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """bfloat16 copy of fl(s * q): nearest bfloat16, ties to even, as the raw
+    16-bit patterns (uint16)."""
+    q = _c(q, np.int8)
+    s = _c(s, np.float32)
+    R, C = q.shape
+    out = np.empty((R, C), np.uint16)
+    _chk(_load().jfo_dequantize_bf16(_p(q), _p(s), R, C, _p(out)), "dequantize_bf16")
+    return out
+
+
+def bf16_round(f: np.ndarray) -> np.ndarray:
+    """Nearest bfloat16 (ties to even) of each finite binary32 value, as uint16 patterns."""
+    f = np.ascontiguousarray(f, dtype=np.float32).ravel()
+    out = np.empty(f.shape, np.uint16)
+    _chk(_load().jfo_bf16_round(_p(f), f.size, _p(out)), "bf16_round")
     return out
 
 

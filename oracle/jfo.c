@@ -32,6 +32,8 @@
  *     then the same per-block requantization;
  *   - residual add of two tensors with the same blocking:
  *     z = fl(fl(s_a * q_a) + fl(s_b * q_b)), then the per-block rule;
+ *   - dequantized value fl(s * q) in binary32; its bfloat16 copy is that
+ *     binary32 value rounded to the nearest bfloat16, ties to even;
  *   - LayerNorm over each row (the hidden dimension): x = fl(s * q);
  *     mean m = (sum x) / n and variance v = (sum (x - m)^2) / n in binary64,
  *     summed in column order; r = 1 / sqrt(v + eps) in binary64;
@@ -137,6 +139,54 @@ int jfo_dequantize(const int8_t *q, const float *s, int64_t rows, int64_t cols, 
     for (int64_t i = 0; i < rows; ++i)
         for (int64_t j = 0; j < cols; ++j)
             x[i * cols + j] = s[(i / JFO_B) * bc + j / JFO_B] * (float)q[i * cols + j];
+    return 0;
+}
+
+/* The bfloat16 nearest to a finite binary32 value f, ties to the even
+ * significand: the two bfloat16 magnitudes around |f| are |f| with its low 16
+ * bits cleared and the next one up (0x7F800000, infinity, past the largest
+ * finite one, which counts as 2^128 for the distance); the closer one is
+ * taken, and on a tie the one whose last kept bit is 0.  Distances are exact
+ * in binary64. */
+static uint16_t bf16_nearest_even(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    const uint32_t sign = u & 0x80000000u, mag = u & 0x7FFFFFFFu;
+    const uint32_t lo = mag & 0xFFFF0000u, hi = lo + 0x10000u;
+    if (lo == mag) return (uint16_t)((sign | lo) >> 16);
+    float flo, fhi;
+    memcpy(&flo, &lo, sizeof flo);
+    memcpy(&fhi, &hi, sizeof fhi);
+    const double a = fabs((double)f);
+    const double dlo = a - (double)flo;
+    const double dhi = (hi == 0x7F800000u ? ldexp(1.0, 128) : (double)fhi) - a;
+    uint32_t r;
+    if (dlo < dhi)
+        r = lo;
+    else if (dhi < dlo)
+        r = hi;
+    else
+        r = (lo & 0x10000u) ? hi : lo;
+    return (uint16_t)((sign | r) >> 16);
+}
+
+/* bfloat16 copy of the dequantized values: nearest-even of fl(s * q). */
+int jfo_dequantize_bf16(const int8_t *q, const float *s, int64_t rows, int64_t cols, uint16_t *x)
+{
+    if (!shape_ok(rows, cols)) return -1;
+    const int64_t bc = cols / JFO_B;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < rows; ++i)
+        for (int64_t j = 0; j < cols; ++j)
+            x[i * cols + j] = bf16_nearest_even(s[(i / JFO_B) * bc + j / JFO_B] * (float)q[i * cols + j]);
+    return 0;
+}
+
+/* Single binary32 -> bfloat16 conversions (for the pins of the rule above). */
+int jfo_bf16_round(const float *f, int64_t n, uint16_t *out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = bf16_nearest_even(f[i]);
     return 0;
 }
 

@@ -14,7 +14,7 @@ import numpy as np
 import pytest
 
 import oracle
-from exact import frac, round_half_even, to_f32
+from exact import floor_log2, frac, round_half_even, to_f32
 from int8_block_quantized_amd import inputs
 
 
@@ -170,3 +170,65 @@ def test_dequantize_is_blockwise_product():
 def test_bad_shapes_rejected():
     with pytest.raises(ValueError):
         oracle.quantize(np.zeros((33, 32), np.float32))
+
+
+def nearest_bf16_exact(v: Fraction) -> Fraction:
+    """The bfloat16 value nearest to v (8 significant bits, binary32's
+    exponent range, ties to the even significand), in exact rationals."""
+    if v == 0:
+        return Fraction(0)
+    sign = -1 if v < 0 else 1
+    a = abs(v)
+    e = max(floor_log2(a), -126)
+    ulp = Fraction(2) ** (e - 7)
+    return sign * round_half_even(a / ulp) * ulp
+
+
+def bf16_value(bits: int) -> Fraction:
+    return frac(np.array([bits << 16], np.uint32).view(np.float32)[0])
+
+
+def test_bf16_round_is_nearest_even_exact():
+    """The oracle's binary32 -> bfloat16 rounding against the nearest-even
+    rule in exact rationals: random values over the whole exponent range,
+    subnormals, and every halfway case (and its two binary32 neighbours) on
+    a grid of significands and exponents."""
+    g = np.random.default_rng(21)
+    f = (g.standard_normal(3000) * np.exp2(g.integers(-140, 120, 3000))).astype(np.float32)
+    ties = []
+    for e in (-133, -126, -20, -1, 0, 1, 7, 60, 126):
+        for m in range(0, 128, 9):
+            half = np.float32(2.0 ** e * (1 + m / 128) + 2.0 ** (e - 8)) if e >= -126 else np.float32(
+                2.0 ** -126 * m / 128 + 2.0 ** (-134))
+            ties += [half, -half, np.nextafter(half, np.float32(0)), np.nextafter(half, np.float32(np.inf))]
+    f = np.concatenate([f, np.array(ties, np.float32), np.array([0.0, -0.0, 1e-45, -1e-45], np.float32)])
+    got = oracle.bf16_round(f)
+    for x, b in zip(f, got):
+        assert bf16_value(int(b)) == nearest_bf16_exact(frac(x)), (x, hex(b))
+
+
+def test_bf16_round_matches_torch_and_overflows():
+    """Library cross-check (torch's CPU conversion rounds to nearest even)
+    on 2^20 random values, plus the overflow edge: the largest binary32
+    rounds up to infinity, the largest bfloat16 stays."""
+    torch = pytest.importorskip("torch")
+    g = np.random.default_rng(22)
+    f = (g.standard_normal(1 << 20) * np.exp2(g.integers(-140, 127, 1 << 20))).astype(np.float32)
+    ref = torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(oracle.bf16_round(f), ref)
+    big = np.array([np.finfo(np.float32).max, 3.3895314e38, -np.finfo(np.float32).max], np.float32)
+    assert list(oracle.bf16_round(big)) == [0x7F80, 0x7F7F, 0xFF80]
+
+
+def test_dequantize_bf16_rounds_the_binary32_product():
+    g = np.random.default_rng(23)
+    q = g.integers(-127, 128, size=(64, 96)).astype(np.int8)
+    s = (g.random((2, 3)) * np.exp2(g.integers(-30, 30, (2, 3)))).astype(np.float32)
+    s[1, 2] = 0.0
+    y32 = (np.repeat(np.repeat(s.astype(np.float64), 32, 0), 32, 1) * q).astype(np.float32)
+    got = oracle.dequantize_bf16(q, s)
+    want = np.array([int(b) for b in oracle.bf16_round(y32)], np.uint16).reshape(q.shape)
+    np.testing.assert_array_equal(got, want)
+    for x, b in zip(y32.ravel()[::37], got.ravel()[::37]):
+        assert bf16_value(int(b)) == nearest_bf16_exact(frac(x))
+    assert not (got[32:, 64:] & 0x7FFF).any()   # a zero scale gives zeros (negative codes: -0)
