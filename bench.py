@@ -21,6 +21,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -664,18 +665,62 @@ def memory_bound_section(reps=20):
         i[0] ^= 1
         jf.gelu_i8(qs[i[0]][0], qs[i[0]][1], qo=qo, so=so)
 
+    y = torch.empty((R, C), dtype=torch.bfloat16, device=dev)
+
+    def dequant():
+        i[0] ^= 1
+        jf.dequantize_block(qs[i[0]][0], qs[i[0]][1], dtype=torch.bfloat16, y=y)
+
     q_us = _time_us(quant, reps)
     g_us = _time_us(gelu, reps)
-    qb, gb = n * (5 + 4 / 1024), n * (2 + 8 / 1024)
-    del xs, x, qs
+    d_us = _time_us(dequant, reps)
+    qb, gb, db = n * (5 + 4 / 1024), n * (2 + 8 / 1024), n * (3 + 4 / 1024)
+    check = gelu_copy_check(x, qs[0][1], *jf.gelu_i8(qs[0][0], qs[0][1]), y)
+    del xs, x, qs, y
     torch.cuda.empty_cache()
     out = {}
-    for name, us, nb in (("quantize", q_us, qb), ("gelu", g_us, gb)):
+    for name, us, nb in (("quantize", q_us, qb), ("gelu", g_us, gb), ("dequantize_bf16", d_us, db)):
         gbs = nb / (us * 1e-6) / 1e9
         out[name] = {"us": round(us, 1), "gbs": round(gbs, 1), "frac_of_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+    out["gelu_bf16_copy_check"] = check
     out["what"] = ("16384x16384 fp32 N(0,1) with 1% of columns x100: jf_quantize_block (fp32 -> INT8 + 32x32 "
-                   "scales), then jf_gelu_i8 on the codes; two input copies used in turn")
+                   "scales), then jf_gelu_i8 on the codes, and jf_dequantize_block of codes to bfloat16 "
+                   "(3 + 4/1024 B per element); two input copies used in turn")
     return out
+
+
+def gelu_copy_check(x, s1, qg, sg, y):
+    """The bfloat16 dequantized copy of the INT8 GELU output against the
+    binary64 GELU of the original fp32 activation (outside any timed region).
+    Per element the data flow's error is bounded by the input quantization
+    (|x - s1 q1| <= s1 (1/2 + 2e-5) with the quotient's rounding, times
+    max |GELU'| < 1.13), the output code rounding (s2 (1/2 + 2e-5)) and the
+    bfloat16 rounding (2^-9 relative, 2^-8 with the binary32 roundings);
+    reported: the largest error over that bound, the largest error in output
+    code units (err / s2) and the normwise relative error."""
+    import torch
+
+    from int8_block_quantized_amd import jetfire as jf
+
+    jf.dequantize_block(qg, sg, dtype=torch.bfloat16, y=y)
+    R, C = x.shape
+    worst_bound = worst_lsb = num = den = 0.0
+    for r0 in range(0, R, 2048):
+        xs = x[r0:r0 + 2048].double()
+        g = 0.5 * xs * torch.special.erfc(-xs / math.sqrt(2.0))
+        yb = y[r0:r0 + 2048].double()
+        e = (yb - g).abs()
+        e1 = s1[r0 // 32:(r0 + 2048) // 32].double().repeat_interleave(32, 0).repeat_interleave(32, 1)
+        e2 = sg[r0 // 32:(r0 + 2048) // 32].double().repeat_interleave(32, 0).repeat_interleave(32, 1)
+        bound = 1.13 * e1 * (0.5 + 2e-5) + e2 * (0.5 + 2e-5) + 2.0 ** -8 * yb.abs() + 1e-30
+        worst_bound = max(worst_bound, float((e / bound).max()))
+        worst_lsb = max(worst_lsb, float((e / torch.where(e2 > 0, e2, torch.ones_like(e2))).max()))
+        num += float((e * e).sum())
+        den += float((g * g).sum())
+        del xs, g, yb, e, e1, e2, bound
+    return {"max_err_over_bound": round(worst_bound, 4), "max_err_output_lsb": round(worst_lsb, 4),
+            "rel_fro": float(f"{math.sqrt(num / den):.4e}"),
+            "what": "bf16(fl(s2 q2)) of jf_gelu_i8's output vs binary64 GELU(x) of the fp32 input"}
 
 
 def main():

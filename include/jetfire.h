@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define JF_ABI_VERSION 4
+#define JF_ABI_VERSION 5
 
 #ifndef JF_API
 #define JF_API __attribute__((visibility("default")))
@@ -105,6 +105,21 @@ typedef enum jf_gran { JF_GRAN_BLOCK = 0, JF_GRAN_TOKEN = 1, JF_GRAN_CHANNEL = 2
  */
 JF_API jf_status jf_quantize_block(jf_dtype xt, const void *x, int64_t ldx, int64_t rows, int64_t cols,
                             int8_t *q, int64_t ldq, float *s, hipStream_t stream);
+
+/*
+ * jf_dequantize_block -- per-block INT8 codes back to high precision.
+ * Pages: "Approach" (INT8 tensors with one scale per 32x32 block); the
+ * dequantized value of code q under block scale s is fl(s*q).
+ *
+ *   q, s  rows x cols codes (ldq) and their scale grid
+ *   yt    JF_F32: y is binary32, y = fl(s*q) exactly as the convention above;
+ *         JF_BF16: y is bfloat16, that binary32 value rounded to the nearest
+ *         bfloat16, ties to even
+ *   y     rows x cols output, leading dimension ldy (elements of yt)
+ * y may not overlap q or s.
+ */
+JF_API jf_status jf_dequantize_block(const int8_t *q, int64_t ldq, const float *s, int64_t rows, int64_t cols,
+                                     jf_dtype yt, void *y, int64_t ldy, hipStream_t stream);
 
 /*
  * jf_gemm_i8_blockscaled -- C[M x N] = op(A)[M x K] . op(B)[K x N] on INT8

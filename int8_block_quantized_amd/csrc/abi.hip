@@ -85,6 +85,21 @@ jf_status jf_requant_block(const float *x, int64_t ldx, int64_t rows, int64_t co
     return jf_quantize_block(JF_F32, x, ldx, rows, cols, q, ldq, s, stream);
 }
 
+jf_status jf_dequantize_block(const int8_t *q, int64_t ldq, const float *s, int64_t rows, int64_t cols,
+                              jf_dtype yt, void *y, int64_t ldy, hipStream_t stream) {
+    if (missing(q, rows, cols) || missing(s, rows, cols) || missing(y, rows, cols)) return JF_ERR_NULL;
+    if (!shape_ok(rows) || !shape_ok(cols)) return JF_ERR_SHAPE;
+    if (yt != JF_F32 && yt != JF_BF16) return JF_ERR_DTYPE;
+    const int64_t elt = yt == JF_F32 ? 4 : 2;
+    if (!ld_ok(ldq, cols, 1) || !ld_ok(ldy, cols, elt)) return JF_ERR_LD;
+    if (!aligned(q, 16) || !aligned(y, 16) || !aligned(s, 4)) return JF_ERR_ALIGN;
+    const Range ry = span(y, rows, cols, ldy, elt);
+    if (overlap(ry, span(q, rows, cols, ldq, 1)) || overlap(ry, span(s, rows / kB, cols / kB, cols / kB, 4)))
+        return JF_ERR_ALIAS;
+    if (rows == 0 || cols == 0) return JF_OK;
+    return hip_status(jf::launch_dequantize(q, ldq, s, rows, cols, yt == JF_BF16, y, ldy, stream));
+}
+
 jf_status jf_gemm_i8_blockscaled(int transA, int transB, int64_t M, int64_t N, int64_t K, const int8_t *A,
                                  int64_t lda, const float *sA, const int8_t *B, int64_t ldb, const float *sB,
                                  jf_out out, void *C, int64_t ldc, float *sC, hipStream_t stream) {

@@ -12,6 +12,8 @@ hipError_t launch_quantize_f32(const float *x, int64_t ldx, int64_t rows, int64_
                                int8_t *q, int64_t ldq, float *s, hipStream_t stream);
 hipError_t launch_quantize_bf16(const uint16_t *x, int64_t ldx, int64_t rows, int64_t cols,
                                 int8_t *q, int64_t ldq, float *s, hipStream_t stream);
+hipError_t launch_dequantize(const int8_t *q, int64_t ldq, const float *s, int64_t rows, int64_t cols, bool bf16,
+                             void *y, int64_t ldy, hipStream_t stream);
 hipError_t launch_gemm(int transA, int transB, int64_t M, int64_t N, int64_t K,
                        const int8_t *A, int64_t lda, const float *sA,
                        const int8_t *B, int64_t ldb, const float *sB,

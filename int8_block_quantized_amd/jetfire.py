@@ -6,8 +6,8 @@ ABI.  torch supplies device memory (outputs are allocated with
 stream).  There is no fallback: if the library is missing, importing this
 module raises.
 
-Names follow the C ABI:  quantize_block, gemm_i8_blockscaled, requant_block,
-gelu_i8, gelu_bwd_i8, add_i8, layernorm_i8, quant_error.  A tensor argument is a 2-D CUDA(HIP) tensor whose last dimension is
+Names follow the C ABI:  quantize_block, dequantize_block, gemm_i8_blockscaled,
+requant_block, gelu_i8, gelu_bwd_i8, add_i8, layernorm_i8, quant_error.  A tensor argument is a 2-D CUDA(HIP) tensor whose last dimension is
 contiguous; its row stride is passed as the leading dimension.
 """
 from __future__ import annotations
@@ -27,7 +27,7 @@ JF_OUT_I8, JF_OUT_F32 = 0, 1
 GRANULARITIES = {"block": 0, "token": 1, "channel": 2, "tensor": 3}
 
 # Every symbol include/jetfire.h declares.
-EXPORTS = ("jf_quantize_block", "jf_gemm_i8_blockscaled", "jf_requant_block", "jf_gelu_i8",
+EXPORTS = ("jf_quantize_block", "jf_dequantize_block", "jf_gemm_i8_blockscaled", "jf_requant_block", "jf_gelu_i8",
            "jf_gelu_bwd_i8", "jf_add_i8", "jf_layernorm_i8", "jf_quant_error", "jf_status_str",
            "jf_abi_version")
 
@@ -47,6 +47,8 @@ def _load() -> ctypes.CDLL:
     lib.jf_quantize_block.restype = cint
     lib.jf_requant_block.argtypes = [ptr, i64, i64, i64, ptr, i64, ptr, ptr]
     lib.jf_requant_block.restype = cint
+    lib.jf_dequantize_block.argtypes = [ptr, i64, ptr, i64, i64, cint, ptr, i64, ptr]
+    lib.jf_dequantize_block.restype = cint
     lib.jf_gemm_i8_blockscaled.argtypes = [cint, cint, i64, i64, i64, ptr, i64, ptr, ptr, i64, ptr,
                                            cint, ptr, i64, ptr, ptr]
     lib.jf_gemm_i8_blockscaled.restype = cint
@@ -142,6 +144,30 @@ def requant_block(x: torch.Tensor, q: torch.Tensor | None = None, s: torch.Tenso
     _check(lib.jf_requant_block(_ptr(x), ldx, R, C, _ptr(q), ldq, _ptr(s), _stream(x.device)),
            "jf_requant_block")
     return q, s
+
+
+def dequantize_block(q: torch.Tensor, s: torch.Tensor, dtype: torch.dtype = torch.float32,
+                     y: torch.Tensor | None = None) -> torch.Tensor:
+    """jf_dequantize_block: int8 codes [R, C] + float32 scales [R/32, C/32]
+    -> float32 fl(s*q), or that value rounded to bfloat16 (``dtype``)."""
+    ldq = _mat(q, "q")
+    if q.dtype != torch.int8:
+        raise ValueError("q must be int8")
+    if dtype == torch.float32:
+        yt = JF_F32
+    elif dtype == torch.bfloat16:
+        yt = JF_BF16
+    else:
+        raise ValueError("dtype must be float32 or bfloat16")
+    R, C = q.shape
+    _scales(s, R, C, "s")
+    y = torch.empty((R, C), dtype=dtype, device=q.device) if y is None else y
+    if y.dtype != dtype:
+        raise ValueError("y must have the requested dtype")
+    ldy = _mat(y, "y")
+    _check(lib.jf_dequantize_block(_ptr(q), ldq, _ptr(s), R, C, yt, _ptr(y), ldy, _stream(q.device)),
+           "jf_dequantize_block")
+    return y
 
 
 def gemm_i8_blockscaled(a: torch.Tensor, sa: torch.Tensor, b: torch.Tensor, sb: torch.Tensor,

@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert jf.abi_version() == 4
+    assert jf.abi_version() == 5
     for st in range(0, 9):
         assert jf.status_str(st) and jf.status_str(st) != "unknown status"
     assert jf.status_str(99) == "unknown status"
@@ -86,6 +86,24 @@ def test_quantize_validation_codes():
     r = jf.lib.jf_requant_block
     assert r(None, 64, 64, 64, qq, 64, s, None) == jf.JF_ERR_NULL
     assert r(x, 64, 64, 64, qq, 64, P(BASE + 0x40), None) == jf.JF_ERR_ALIAS
+
+
+def test_dequantize_validation_codes():
+    d = jf.lib.jf_dequantize_block
+    q, s, y = P(BASE), P(BASE + 0x10000000), P(BASE + 0x20000000)
+    assert d(q, 64, None, 64, 64, jf.JF_F32, y, 64, None) == jf.JF_ERR_NULL
+    assert d(q, 64, s, 64, 64, jf.JF_BF16, None, 64, None) == jf.JF_ERR_NULL
+    assert d(q, 64, s, 72, 64, jf.JF_F32, y, 64, None) == jf.JF_ERR_SHAPE
+    assert d(q, 64, s, 64, 64, 2, y, 64, None) == jf.JF_ERR_DTYPE
+    assert d(q, 48, s, 64, 64, jf.JF_F32, y, 64, None) == jf.JF_ERR_LD            # below the row length
+    assert d(q, 64, s, 64, 64, jf.JF_F32, y, 66, None) == jf.JF_ERR_LD            # 264-byte pitch
+    assert d(q, 64, s, 64, 64, jf.JF_BF16, y, 68, None) == jf.JF_ERR_LD           # 136-byte pitch
+    assert d(P(BASE + 8), 64, s, 64, 64, jf.JF_F32, y, 64, None) == jf.JF_ERR_ALIGN
+    assert d(q, 64, s, 64, 64, jf.JF_F32, P(BASE + 0x20000008), 64, None) == jf.JF_ERR_ALIGN
+    assert d(q, 64, P(BASE + 0x10000002), 64, 64, jf.JF_F32, y, 64, None) == jf.JF_ERR_ALIGN
+    assert d(q, 64, s, 64, 64, jf.JF_F32, P(BASE + 0x100), 64, None) == jf.JF_ERR_ALIAS     # over the codes
+    assert d(q, 64, s, 64, 64, jf.JF_BF16, P(BASE + 0x10000000 - 8192 + 16), 64, None) == jf.JF_ERR_ALIAS  # over s
+    assert d(q, 64, s, 0, 64, jf.JF_F32, None, 64, None) == jf.JF_OK                # empty
 
 
 def test_gelu_validation_codes():
