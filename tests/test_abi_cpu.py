@@ -197,3 +197,24 @@ def test_binding_refuses_host_tensors():
     torch = pytest.importorskip("torch")
     with pytest.raises(ValueError):
         jf.quantize_block(torch.zeros(32, 32))
+
+
+def test_binding_fails_loudly_without_the_library(tmp_path, monkeypatch):
+    """No fallback: with libjetfire.so absent the binding's loader raises
+    instead of handing out another implementation."""
+    monkeypatch.setattr(jf, "LIB_PATH", str(tmp_path / "libjetfire.so"))
+    with pytest.raises(ImportError, match="not built"):
+        jf._load()
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU; --gpus above 1 exits with a message before
+    touching a device."""
+    import subprocess
+    import sys
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    res = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                         text=True, timeout=120)
+    assert res.returncode == 2
+    assert "one GPU" in res.stderr and not res.stdout.strip()
