@@ -24,6 +24,10 @@
 4. The 256 x 256 tile of the gradient layouts on a ragged 8224 x 4192 grid:
    every element with the exact construction, the edge blocks against the
    oracle with real codes and scales.
+5. The GPT2-base linear (4096 tokens, 768 -> 3072) and the GPT2-medium MLP
+   (8192 tokens, 1024 -> 4096 -> 1024): every GEMM on its workload's data,
+   every element of both outputs against the oracle (grids of fewer than
+   512 main tiles run the 64 x 128 tile, the others the 128 x 256 one).
 
 The binary32 bar is |gpu - oracle| <= 1e-5 * sum_k |sigma_k P_k| per element
 and 1e-5 normwise; the bound is evaluated on the blocks that differ (none is
@@ -179,6 +183,25 @@ def test_hidden4096_every_element_exact(label):
     del exp32
     frac, srel = assert_requant_close(host(q), host(s), rq, rs, label)
     note(f"  {M * N} elements: f32 exact everywhere; i8 code diffs {frac:.2e}, scale rel {srel:.1e}")
+
+
+GPT2 = [(w, g[0]) for w in ("gpt2_base", "gpt2_medium_mlp") for g in inputs.WORKLOADS[w]().gemms()]
+
+
+@pytest.mark.parametrize("wname,label", GPT2)
+def test_gpt2_workloads_every_element(wname, label):
+    wl = inputs.WORKLOADS[wname]()
+    _, ta, tb, M, N, K, an, bn = {g[0]: g for g in wl.gemms()}[label]
+    qa, sa, oqa, osa = quantized(wl, an)
+    qb, sb, oqb, osb = quantized(wl, bn)
+    note(f"{wl.name} {label}: M={M} N={N} K={K} tA={ta} tB={tb}, every element")
+    c, q, s = run_gemm(qa, sa, qb, sb, ta, tb, M, N)
+    gc, gq, gs = host(c), host(q), host(s)
+    ref = oracle.gemm_f32(oqa, osa, oqb, osb, ta=ta, tb=tb)
+    exact = check_f32(gc, ref, oqa, osa, oqb, osb, ta, tb, lambda r: r, f"{label} f32")
+    rq, rs = oracle.requant(ref)
+    frac, srel = assert_requant_close(gq, gs, rq, rs, f"{label} i8")
+    note(f"  f32 bit-exact {exact:.6f}, i8 code diffs {frac:.2e}, scale rel {srel:.1e}")
 
 
 @pytest.mark.parametrize("ta,tb", [(0, 1), (1, 0), (1, 1)])
