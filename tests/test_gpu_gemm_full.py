@@ -24,7 +24,9 @@
 4. The 256 x 256 tile of the gradient layouts on a ragged 8224 x 4192 grid:
    every element with the exact construction, the edge blocks against the
    oracle with real codes and scales.
-5. The GPT2-base linear (4096 tokens, 768 -> 3072) and the GPT2-medium MLP
+5. 64-bit load offsets on the two large tiles: one operand with a leading
+   dimension of 2^23 + 64 bytes, every element with the exact construction.
+6. The GPT2-base linear (4096 tokens, 768 -> 3072) and the GPT2-medium MLP
    (8192 tokens, 1024 -> 4096 -> 1024): every GEMM on its workload's data,
    every element of both outputs against the oracle (grids of fewer than
    512 main tiles run the 64 x 128 tile, the others the 128 x 256 one).
@@ -182,6 +184,59 @@ def test_hidden4096_every_element_exact(label):
     rq, rs = oracle.requant(host(exp32))
     del exp32
     frac, srel = assert_requant_close(host(q), host(s), rq, rs, label)
+    note(f"  {M * N} elements: f32 exact everywhere; i8 code diffs {frac:.2e}, scale rel {srel:.1e}")
+
+
+def exact_expected(A, sA, B, sB, ta, tb):
+    """float64 product of the dequantized operands (exact for the small-code
+    construction) and its binary32 form, on the device."""
+    Ad = torch.from_numpy(oracle.dequantize(A, sA)).to(DEV).double()
+    Bd = torch.from_numpy(oracle.dequantize(B, sB)).to(DEV).double()
+    exp = torch.matmul(Ad.t().contiguous() if ta else Ad, Bd.t().contiguous() if tb else Bd)
+    del Ad, Bd
+    assert float(exp.abs().max()) < 2.0 ** 18
+    exp32 = exp.float()
+    assert torch.equal(exp32.double(), exp), "expected value not exact in binary32"
+    return exp32
+
+
+@pytest.mark.parametrize("case", ["main-tile-fwd", "big-tile-wgrad"])
+def test_wide_leading_dimension_large_tiles(case):
+    """Per-lane load offsets past 32 bits select the kernels' 64-bit address
+    path when (ld + 1) * tile edge >= 2^31; with a 256-element tile edge a
+    leading dimension of 2^23 + 64 bytes does it.  The forward layout on a
+    4096 x 4096 x 256 grid (512 main tiles) with B stored 256 x ld (2.1 GB),
+    and the weight-gradient layout on 8192 x 16384 x 2048 (2048 tiles of
+    256 x 256, 64 k-blocks) with A stored 2048 x ld (17 GB of HBM); the
+    operand sits at the end of each row.  Every element, exact construction."""
+    if case == "main-tile-fwd":
+        ta, tb, M, N, K = 0, 0, 4096, 4096, 256
+    else:
+        ta, tb, M, N, K = 1, 0, 8192, 16384, 2048
+    seed = 950 + len(case)
+    A = stored(inputs.small_codes(seed, 0, 0, M, K, 2), ta)
+    B = stored(inputs.small_codes(seed, 0, 1, K, N, 2), tb)
+    sA = stored(inputs.pow2_scales(seed, 0, 2, M // 32, K // 32, -1, 1), ta)
+    sB = stored(inputs.pow2_scales(seed, 0, 3, K // 32, N // 32, -1, 1), tb)
+    wide = B if case == "main-tile-fwd" else A
+    ld = (1 << 23) + 64
+    note(f"wide ld {case}: {M}x{N}x{K} tA={ta} tB={tb}, a {wide.shape[0]} x {ld} operand "
+         f"({wide.shape[0] * ld / 2**30:.1f} GiB)")
+    big = torch.empty((wide.shape[0], ld), dtype=torch.int8, device=DEV)
+    view = big[:, ld - wide.shape[1]:]
+    view.copy_(dev(wide))
+    qa, qb = (dev(A), view) if case == "main-tile-fwd" else (view, dev(B))
+    c, q, s = run_gemm(qa, dev(sA), qb, dev(sB), ta, tb, M, N)
+    torch.cuda.synchronize()
+    del qa, qb, view, big
+    torch.cuda.empty_cache()
+    exp32 = exact_expected(A, sA, B, sB, ta, tb)
+    assert not torch.isnan(c).any(), f"{case}: unwritten (NaN) outputs"
+    nbad = int((c != exp32).sum())
+    assert nbad == 0, f"{case}: {nbad} binary32 outputs differ from the exact product"
+    del c
+    rq, rs = oracle.requant(host(exp32))
+    frac, srel = assert_requant_close(host(q), host(s), rq, rs, case)
     note(f"  {M * N} elements: f32 exact everywhere; i8 code diffs {frac:.2e}, scale rel {srel:.1e}")
 
 
