@@ -9,8 +9,9 @@
 //
 // 32x32 blocks take one pass.  Rows, columns and the tensor take three
 // launches after clearing: group maxima (non-negative binary32 maxima
-// combined as bit patterns with atomic integer max), maxima -> scales, then
-// codes and errors.  Error sums are per-lane binary64, reduced per
+// combined as bit patterns with atomic integer max; column maxima walk down
+// the bands, the others along them), maxima -> scales, then codes and
+// errors.  Error sums are per-lane binary64, reduced per
 // workgroup, one atomic add each.
 //
 // Element mapping: the quantizer's band workgroup.  A workgroup covers one
@@ -30,6 +31,10 @@ constexpr int kRows = 8;                    // rows per wavefront
 constexpr int kWaves = kBlock / kRows;      // 4 wavefronts
 constexpr int kSegBlocks = 8;               // blocks per 1 KiB segment of fp32
 constexpr int kMaxSegPerWG = 8;   // segments per workgroup, in turn (at most)
+#ifndef JF_QE_BPW
+#define JF_QE_BPW 4
+#endif
+constexpr int kMaxBandsPerWG = JF_QE_BPW;   // bands per column-maxima workgroup (at most)
 constexpr int64_t kMaxGridX = 1 << 20, kMaxGridY = 1 << 15;
 
 enum { kBlockG = 0, kToken = 1, kChannel = 2, kTensor = 3 };
@@ -80,7 +85,7 @@ __device__ __forceinline__ void wg_sum_add(double acc, double *sse) {
 template <int G>
 __global__ __launch_bounds__(64 * kWaves) void k_qe_max(const float *__restrict__ x, int64_t ldx, int nbc, int nseg,
                                                         int spw, int sg0, int band0, uint32_t *__restrict__ mx) {
-    __shared__ uint32_t wmax[2][kWaves][kWave * 4];
+    __shared__ uint32_t wmax[kWaves];
     const int lane = threadIdx.x & (kWave - 1), wave = wave_id_uniform();
     const int band = band0 + blockIdx.y, seg_first = (sg0 + blockIdx.x) * spw;
     float tmax = 0.0f;                                   // tensor: running maximum
@@ -96,7 +101,8 @@ __global__ __launch_bounds__(64 * kWaves) void k_qe_max(const float *__restrict_
             for (int i = 0; i < kRows; ++i)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) tmax = fmaxf(tmax, t.valid ? fabsf(t.v[i][e]) : 0.0f);
-        } else if constexpr (G == kToken) {
+        } else {
+            static_assert(G == kToken, "column maxima: k_qe_colmax");
             // row i of the wavefront: max over the lane's 4 values, then the wavefront
 #pragma unroll
             for (int i = 0; i < kRows; ++i) {
@@ -106,35 +112,56 @@ __global__ __launch_bounds__(64 * kWaves) void k_qe_max(const float *__restrict_
                 const uint32_t u = __float_as_uint(wave_max_nonneg(t.valid ? m : 0.0f));
                 if (lane == 0) atomicMax(mx + t.row0 + i, u);
             }
-        } else {
-            // columns col0..col0+3: max over the wavefront's 8 rows, then over
-            // the four wavefronts through LDS (two buffers: one barrier per
-            // segment), one atomic per column
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                float m = 0.0f;
-#pragma unroll
-                for (int i = 0; i < kRows; ++i) m = fmaxf(m, fabsf(t.v[i][e]));
-                wmax[j & 1][wave][4 * lane + e] = __float_as_uint(m);
-            }
-            __syncthreads();
-            if (wave == 0 && t.valid) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int c = 4 * lane + e;
-                    atomicMax(mx + t.col0 + e, max(max(wmax[j & 1][0][c], wmax[j & 1][1][c]),
-                                                   max(wmax[j & 1][2][c], wmax[j & 1][3][c])));
-                }
-            }
         }
         t = nt;
     }
     if constexpr (G == kTensor) {
         const uint32_t wm = __float_as_uint(wave_max_nonneg(tmax));
-        if (lane == 0) wmax[0][wave][0] = wm;
+        if (lane == 0) wmax[wave] = wm;
         __syncthreads();
-        if (threadIdx.x == 0)
-            atomicMax(mx, max(max(wmax[0][0][0], wmax[0][1][0]), max(wmax[0][2][0], wmax[0][3][0])));
+        if (threadIdx.x == 0) atomicMax(mx, max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3])));
+    }
+}
+
+// Column maxima.  A workgroup takes one 1 KiB segment (256 columns) and bpw
+// consecutive bands, walking down them with the next band's loads issued
+// before the current one is reduced; each lane keeps the running maxima of
+// its four columns over its rows, the four wavefronts combine them through
+// LDS once, and the workgroup ends in one atomic per column (lane l of the
+// first wavefront takes columns l, l + 64, l + 128, l + 192, so each atomic
+// instruction covers 256 contiguous bytes).  Walking along the band instead
+// (as the row and tensor maxima do) would cost a barrier and 256 atomics per
+// segment.
+__global__ __launch_bounds__(64 * kWaves) void k_qe_colmax(const float *__restrict__ x, int64_t ldx, int nbc,
+                                                           int nbr, int bpw, int sg0, int bg0,
+                                                           uint32_t *__restrict__ mx) {
+    __shared__ uint32_t cmax[kWaves][kWave * 4];
+    const int lane = threadIdx.x & (kWave - 1), wave = wave_id_uniform();
+    const int seg = sg0 + blockIdx.x, band_first = (bg0 + blockIdx.y) * bpw;
+    const int band_last = min(band_first + bpw, nbr) - 1;
+    float m[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    Tile t = load_tile(x, ldx, nbc, seg, band_first);
+#pragma unroll 1
+    for (int j = band_first; j <= band_last; ++j) {
+        // the next band's loads go out first; after the last band they re-read it
+        const Tile nt = load_tile(x, ldx, nbc, seg, min(j + 1, band_last));
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int i = 0; i < kRows; ++i) m[e] = fmaxf(m[e], fabsf(t.v[i][e]));
+        t = nt;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) cmax[wave][4 * lane + e] = __float_as_uint(m[e]);   // column 4 lane + e
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int c = lane + kWave * e;                     // column of the segment
+            if (seg * kSegBlocks + c / kBlock < nbc)
+                atomicMax(mx + (int64_t)seg * kSegBlocks * kBlock + c,
+                          max(max(cmax[0][c], cmax[1][c]), max(cmax[2][c], cmax[3][c])));
+        }
     }
 }
 
@@ -301,14 +328,25 @@ hipError_t launch_g(const float *x, int64_t ldx, int64_t rows, int64_t cols, flo
     // written whole by the one-pass kernel)
     hipLaunchKernelGGL(k_qe_init, dim3((unsigned)((ng + 256) / 256)), dim3(256), 0, stream, mx, ng, sse);
     if (nbr == 0 || nbc == 0) return hipGetLastError();
-    for_grid(nbr, nsg, [&](int64_t b0, int64_t s0, dim3 grid) {
-        if constexpr (G == kBlockG)
-            hipLaunchKernelGGL(k_qe_block, grid, dim3(64 * kWaves), 0, stream, x, ldx, (int)nbc, (int)nseg, spw,
-                               (int)s0, (int)b0, s, sse);
-        else
-            hipLaunchKernelGGL(k_qe_max<G>, grid, dim3(64 * kWaves), 0, stream, x, ldx, (int)nbc, (int)nseg, spw,
+    if constexpr (G == kChannel) {
+        // bands per workgroup: as many (up to kMaxBandsPerWG) as keep at least 1024 workgroups
+        int bpw = kMaxBandsPerWG;
+        while (bpw > 1 && nseg * ((nbr + bpw - 1) / bpw) < 1024) bpw /= 2;
+        const int64_t nbg = (nbr + bpw - 1) / bpw;
+        for_grid(nbg, nseg, [&](int64_t b0, int64_t s0, dim3 grid) {
+            hipLaunchKernelGGL(k_qe_colmax, grid, dim3(64 * kWaves), 0, stream, x, ldx, (int)nbc, (int)nbr, bpw,
                                (int)s0, (int)b0, mx);
-    });
+        });
+    } else {
+        for_grid(nbr, nsg, [&](int64_t b0, int64_t s0, dim3 grid) {
+            if constexpr (G == kBlockG)
+                hipLaunchKernelGGL(k_qe_block, grid, dim3(64 * kWaves), 0, stream, x, ldx, (int)nbc, (int)nseg, spw,
+                                   (int)s0, (int)b0, s, sse);
+            else
+                hipLaunchKernelGGL(k_qe_max<G>, grid, dim3(64 * kWaves), 0, stream, x, ldx, (int)nbc, (int)nseg,
+                                   spw, (int)s0, (int)b0, mx);
+        });
+    }
     if constexpr (G != kBlockG) {
         hipLaunchKernelGGL(k_qe_scale, dim3((unsigned)((ng + 255) / 256)), dim3(256), 0, stream, mx, ng);
         for_grid(nbr, nsg, [&](int64_t b0, int64_t s0, dim3 grid) {
