@@ -155,41 +155,9 @@ def test_hidden4096_every_32nd_block_row(label):
          f"({int(round(frac * gq.size))} of {gq.size}), scale rel {srel:.1e}")
 
 
-@pytest.mark.parametrize("label", list(H4096))
-def test_hidden4096_every_element_exact(label):
-    _, ta, tb, M, N, K, _, _ = H4096[label]
-    seed = 800 + zlib.crc32(label.encode()) % 1000
-    A = stored(inputs.small_codes(seed, 0, 0, M, K, 2), ta)
-    B = stored(inputs.small_codes(seed, 0, 1, K, N, 2), tb)
-    sA = stored(inputs.pow2_scales(seed, 0, 2, M // 32, K // 32, -1, 1), ta)
-    sB = stored(inputs.pow2_scales(seed, 0, 3, K // 32, N // 32, -1, 1), tb)
-    note(f"{label}: every element, M={M} N={N} K={K} tA={ta} tB={tb}")
-    c, q, s = run_gemm(dev(A), dev(sA), dev(B), dev(sB), ta, tb, M, N)
-    # exact expected value: float64 product of the dequantized operands
-    Ad = torch.from_numpy(oracle.dequantize(A, sA)).to(DEV).double()
-    Bd = torch.from_numpy(oracle.dequantize(B, sB)).to(DEV).double()
-    Ad = Ad.t().contiguous() if ta else Ad
-    Bd = Bd.t().contiguous() if tb else Bd
-    exp = torch.matmul(Ad, Bd)
-    del Ad, Bd
-    assert float(exp.abs().max()) < 2.0 ** 18
-    exp32 = exp.float()
-    assert torch.equal(exp32.double(), exp), "expected value not exact in binary32"
-    del exp
-    bad = (c != exp32)
-    nbad = int(bad.sum())
-    assert not torch.isnan(c).any(), f"{label}: unwritten (NaN) outputs"
-    assert nbad == 0, f"{label}: {nbad} binary32 outputs differ from the exact product"
-    del bad, c
-    rq, rs = oracle.requant(host(exp32))
-    del exp32
-    frac, srel = assert_requant_close(host(q), host(s), rq, rs, label)
-    note(f"  {M * N} elements: f32 exact everywhere; i8 code diffs {frac:.2e}, scale rel {srel:.1e}")
-
-
 def exact_expected(A, sA, B, sB, ta, tb):
-    """float64 product of the dequantized operands (exact for the small-code
-    construction) and its binary32 form, on the device."""
+    """The float64 product of the dequantized operands, on the device, as
+    binary32 (checked to be exact in both: the small-code construction)."""
     Ad = torch.from_numpy(oracle.dequantize(A, sA)).to(DEV).double()
     Bd = torch.from_numpy(oracle.dequantize(B, sB)).to(DEV).double()
     exp = torch.matmul(Ad.t().contiguous() if ta else Ad, Bd.t().contiguous() if tb else Bd)
@@ -198,6 +166,37 @@ def exact_expected(A, sA, B, sB, ta, tb):
     exp32 = exp.float()
     assert torch.equal(exp32.double(), exp), "expected value not exact in binary32"
     return exp32
+
+
+def small_code_operands(seed, M, N, K, ta, tb):
+    """Codes in [-2, 2] and scales in {1/2, 1, 2}, in stored orientation."""
+    A = stored(inputs.small_codes(seed, 0, 0, M, K, 2), ta)
+    B = stored(inputs.small_codes(seed, 0, 1, K, N, 2), tb)
+    sA = stored(inputs.pow2_scales(seed, 0, 2, M // 32, K // 32, -1, 1), ta)
+    sB = stored(inputs.pow2_scales(seed, 0, 3, K // 32, N // 32, -1, 1), tb)
+    return A, sA, B, sB
+
+
+def check_exact(c, q, s, exp32, what):
+    """Every binary32 output equals the exact product; the INT8 output is
+    the oracle's requantization of it (to the INT8 bar)."""
+    assert not torch.isnan(c).any(), f"{what}: unwritten (NaN) outputs"
+    nbad = int((c != exp32).sum())
+    assert nbad == 0, f"{what}: {nbad} binary32 outputs differ from the exact product"
+    rq, rs = oracle.requant(host(exp32))
+    return assert_requant_close(host(q), host(s), rq, rs, what)
+
+
+@pytest.mark.parametrize("label", list(H4096))
+def test_hidden4096_every_element_exact(label):
+    _, ta, tb, M, N, K, _, _ = H4096[label]
+    seed = 800 + zlib.crc32(label.encode()) % 1000
+    A, sA, B, sB = small_code_operands(seed, M, N, K, ta, tb)
+    note(f"{label}: every element, M={M} N={N} K={K} tA={ta} tB={tb}")
+    c, q, s = run_gemm(dev(A), dev(sA), dev(B), dev(sB), ta, tb, M, N)
+    exp32 = exact_expected(A, sA, B, sB, ta, tb)
+    frac, srel = check_exact(c, q, s, exp32, label)
+    note(f"  {M * N} elements: f32 exact everywhere; i8 code diffs {frac:.2e}, scale rel {srel:.1e}")
 
 
 @pytest.mark.parametrize("case", ["main-tile-fwd", "big-tile-wgrad"])
@@ -213,11 +212,7 @@ def test_wide_leading_dimension_large_tiles(case):
         ta, tb, M, N, K = 0, 0, 4096, 4096, 256
     else:
         ta, tb, M, N, K = 1, 0, 8192, 16384, 2048
-    seed = 950 + len(case)
-    A = stored(inputs.small_codes(seed, 0, 0, M, K, 2), ta)
-    B = stored(inputs.small_codes(seed, 0, 1, K, N, 2), tb)
-    sA = stored(inputs.pow2_scales(seed, 0, 2, M // 32, K // 32, -1, 1), ta)
-    sB = stored(inputs.pow2_scales(seed, 0, 3, K // 32, N // 32, -1, 1), tb)
+    A, sA, B, sB = small_code_operands(950 + len(case), M, N, K, ta, tb)
     wide = B if case == "main-tile-fwd" else A
     ld = (1 << 23) + 64
     note(f"wide ld {case}: {M}x{N}x{K} tA={ta} tB={tb}, a {wide.shape[0]} x {ld} operand "
@@ -231,12 +226,7 @@ def test_wide_leading_dimension_large_tiles(case):
     del qa, qb, view, big
     torch.cuda.empty_cache()
     exp32 = exact_expected(A, sA, B, sB, ta, tb)
-    assert not torch.isnan(c).any(), f"{case}: unwritten (NaN) outputs"
-    nbad = int((c != exp32).sum())
-    assert nbad == 0, f"{case}: {nbad} binary32 outputs differ from the exact product"
-    del c
-    rq, rs = oracle.requant(host(exp32))
-    frac, srel = assert_requant_close(host(q), host(s), rq, rs, case)
+    frac, srel = check_exact(c, q, s, exp32, case)
     note(f"  {M * N} elements: f32 exact everywhere; i8 code diffs {frac:.2e}, scale rel {srel:.1e}")
 
 
@@ -268,24 +258,12 @@ def test_big_tile_ragged_every_element(ta, tb):
     and the edge blocks against the oracle with real codes and scales."""
     M, N, K = 8224, 4192, 8192
     seed = 900 + 2 * ta + tb
-    A = stored(inputs.small_codes(seed, 0, 0, M, K, 2), ta)
-    B = stored(inputs.small_codes(seed, 0, 1, K, N, 2), tb)
-    sA = stored(inputs.pow2_scales(seed, 0, 2, M // 32, K // 32, -1, 1), ta)
-    sB = stored(inputs.pow2_scales(seed, 0, 3, K // 32, N // 32, -1, 1), tb)
+    A, sA, B, sB = small_code_operands(seed, M, N, K, ta, tb)
     note(f"big tile ragged: {M}x{N}x{K} tA={ta} tB={tb}, every element")
     c, q, s = run_gemm(dev(A), dev(sA), dev(B), dev(sB), ta, tb, M, N)
-    Ad = torch.from_numpy(oracle.dequantize(A, sA)).to(DEV).double()
-    Bd = torch.from_numpy(oracle.dequantize(B, sB)).to(DEV).double()
-    exp = torch.matmul(Ad.t().contiguous() if ta else Ad, Bd.t().contiguous() if tb else Bd)
-    del Ad, Bd
-    exp32 = exp.float()
-    assert torch.equal(exp32.double(), exp)
-    assert not torch.isnan(c).any()
-    nbad = int((c != exp32).sum())
-    assert nbad == 0, f"{nbad} binary32 outputs differ from the exact product"
-    rq, rs = oracle.requant(host(exp32))
-    frac, srel = assert_requant_close(host(q), host(s), rq, rs, "big tile ragged (exact)")
-    del c, q, s, exp, exp32
+    exp32 = exact_expected(A, sA, B, sB, ta, tb)
+    frac, srel = check_exact(c, q, s, exp32, "big tile ragged (exact)")
+    del c, q, s, exp32
     # real codes and scales on the ragged edge blocks
     A = stored(inputs.codes(seed, 1, 0, M, K), ta)
     B = stored(inputs.codes(seed, 1, 1, K, N), tb)
