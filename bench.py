@@ -614,10 +614,21 @@ def small_configs_section(reps=50):
     ops = 2 * 256 ** 3
     for key, fn in (("tiny_i8_out_us", tiny_i8), ("tiny_f32_out_requant_us", tiny_f32)):
         out[key] = round(_time_us(fn, reps), 2)
+    # the same three calls captured once in a HIP graph and replayed (no host work per kernel)
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        tiny_i8()
+    torch.cuda.current_stream().wait_stream(side)
+    with torch.cuda.graph(graph):
+        tiny_i8()
+    out["tiny_i8_out_graph_us"] = round(_time_us(graph.replay, reps), 2)
     out["tiny_gemm_i8_us"] = round(_time_us(lambda: jf.gemm_i8_blockscaled(qx, sx, qw, sw, c=qy, sc=sy), reps), 2)
     out["tiny_gemm_tops"] = round(ops / (out["tiny_gemm_i8_us"] * 1e-6) / 1e12, 2)
-    out["tiny_what"] = ("tiny forward 256x256x256: quantize X and W, GEMM with INT8 output (i8_out); or binary32 "
-                        "output then jf_requant_block (f32_out_requant); the GEMM alone (gemm_i8)")
+    out["tiny_what"] = ("tiny forward 256x256x256: quantize X and W, GEMM with INT8 output (i8_out; i8_out_graph: "
+                        "the three calls replayed from a captured HIP graph); or binary32 output then "
+                        "jf_requant_block (f32_out_requant); the GEMM alone (gemm_i8)")
     wl = inputs.gpt2_base_linear()
     fp = {n: torch.from_numpy(wl.make(n)).to(dev) for n in ("X", "W", "dY")}
     q = {n: jf.quantize_block(t) for n, t in fp.items()}
