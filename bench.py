@@ -625,10 +625,32 @@ def small_configs_section(reps=50):
         tiny_i8()
     out["tiny_i8_out_graph_us"] = round(_time_us(graph.replay, reps), 2)
     out["tiny_gemm_i8_us"] = round(_time_us(lambda: jf.gemm_i8_blockscaled(qx, sx, qw, sw, c=qy, sc=sy), reps), 2)
-    out["tiny_gemm_tops"] = round(ops / (out["tiny_gemm_i8_us"] * 1e-6) / 1e12, 2)
+    # the same calls straight through the C ABI with prepared arguments: no per-call Python argument checks,
+    # so the time is the kernels' own (the binding's checks cost several microseconds per call)
+    import ctypes
+
+    p = lambda t: ctypes.c_void_p(t.data_ptr())
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    a_qx = (jf.JF_F32, p(x), 256, 256, 256, p(qx), 256, p(sx), st)
+    a_qw = (jf.JF_F32, p(w), 256, 256, 256, p(qw), 256, p(sw), st)
+    a_mm = (0, 0, 256, 256, 256, p(qx), 256, p(sx), p(qw), 256, p(sw), jf.JF_OUT_I8, p(qy), 256, p(sy), st)
+
+    def tiny_abi():
+        jf.lib.jf_quantize_block(*a_qx)
+        jf.lib.jf_quantize_block(*a_qw)
+        jf.lib.jf_gemm_i8_blockscaled(*a_mm)
+
+    for fn, args in ((jf.lib.jf_quantize_block, a_qx), (jf.lib.jf_quantize_block, a_qw),
+                     (jf.lib.jf_gemm_i8_blockscaled, a_mm)):
+        if fn(*args) != jf.JF_OK:
+            raise RuntimeError(f"{fn.__name__}: {jf.status_str(fn(*args))}")
+    out["tiny_i8_out_abi_us"] = round(_time_us(tiny_abi, reps), 2)
+    out["tiny_gemm_i8_abi_us"] = round(_time_us(lambda: jf.lib.jf_gemm_i8_blockscaled(*a_mm), reps), 2)
+    out["tiny_gemm_tops"] = round(ops / (out["tiny_gemm_i8_abi_us"] * 1e-6) / 1e12, 2)
     out["tiny_what"] = ("tiny forward 256x256x256: quantize X and W, GEMM with INT8 output (i8_out; i8_out_graph: "
                         "the three calls replayed from a captured HIP graph); or binary32 output then "
-                        "jf_requant_block (f32_out_requant); the GEMM alone (gemm_i8)")
+                        "jf_requant_block (f32_out_requant); the GEMM alone (gemm_i8); *_abi: the same calls made "
+                        "directly through the C ABI with prepared arguments (no Python argument checks)")
     wl = inputs.gpt2_base_linear()
     fp = {n: torch.from_numpy(wl.make(n)).to(dev) for n in ("X", "W", "dY")}
     q = {n: jf.quantize_block(t) for n, t in fp.items()}
