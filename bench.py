@@ -192,6 +192,16 @@ def read_traffic():
     return out
 
 
+def profile_traffic(family: str):
+    """HBM bytes per launch of a GEMM kernel family from the committed counter
+    summary, or None when that summary was taken on other GEMM sources (its
+    source_digest differs) or does not list the family."""
+    tr = read_traffic()
+    if tr and tr.get("source_digest") == source_digest() and f"traffic[{family}]" in tr:
+        return int(tr[f"traffic[{family}]"])
+    return None
+
+
 def source_digest() -> str:
     h = hashlib.sha256()
     for f in ("csrc/gemm.hip", "csrc/jf_tile_order.h", "csrc/jf_device.h", "_build.py"):   # the kernel, how it is compiled
@@ -834,10 +844,7 @@ def main():
     roof.update({"kernel": dom_name, "achieved": round(achieved, 2),
                  "frac": round(achieved / roof["peak"], 4),
                  "avg_launch_us": round(dom["ms"] / dom["launches"] * 1e3, 2),
-                 "launches_per_step": dom["launches"], "traffic": None})
-    tr = read_traffic()
-    if tr and tr.get("source_digest") == source_digest() and f"traffic[{dom_name}]" in tr:
-        roof["traffic"] = int(tr[f"traffic[{dom_name}]"])
+                 "launches_per_step": dom["launches"], "traffic": profile_traffic(dom_name)})
 
     gemm_ms = sum(per[l] for l, m in step.meta.items() if m["kind"] == "gemm")
     value = step.gemm_ops / (ms_step * 1e-3) / 1e12
