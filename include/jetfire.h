@@ -50,7 +50,10 @@
  *    hands out empty tensors, and an empty output or a K = 0 contraction has
  *    a well-defined result.  JF_ERR_ARG, for flags and granularities out of
  *    range, is likewise an addition to the shape and pointer codes.)
- *  - Inputs must be finite; NaN or Inf inputs give unspecified outputs.
+ *  - Inputs must be finite; NaN or Inf inputs give unspecified outputs, and
+ *    so do finite inputs whose binary32 results overflow (a GEMM sum, a
+ *    residual add or a dequantized value beyond the binary32 range; the
+ *    bfloat16 dequantized copy rounds such values to infinity).
  *  - Entry points keep no state and are safe to call from several threads.
  */
 #ifndef JETFIRE_H
