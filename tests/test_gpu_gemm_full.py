@@ -26,7 +26,10 @@
    oracle with real codes and scales.
 5. 64-bit load offsets on the two large tiles: one operand with a leading
    dimension of 2^23 + 64 bytes, every element with the exact construction.
-6. The GPT2-base linear (4096 tokens, 768 -> 3072) and the GPT2-medium MLP
+6. Shapes on both sides of every tile-selection switch (grid sizes, the
+   256 x 256 tile's work threshold, odd k-block counts), every element with
+   the exact construction.
+7. The GPT2-base linear (4096 tokens, 768 -> 3072) and the GPT2-medium MLP
    (8192 tokens, 1024 -> 4096 -> 1024): every GEMM on its workload's data,
    every element of both outputs against the oracle (grids of fewer than
    512 main tiles run the 64 x 128 tile, the others the 128 x 256 one).
@@ -280,3 +283,30 @@ def test_big_tile_ragged_every_element(ta, tb):
                                         np.array([gs[I, J] for I, J in blks]), oq, os_, "big tile ragged edges")
     note(f"  exact: f32 exact everywhere, i8 code diffs {frac:.2e}; {len(blks)} edge blocks with real scales: "
          f"f32 bit-exact, i8 code diffs {frac2:.2e}")
+
+
+# Shapes on both sides of every dispatch switch: the 64 x 128 tile below 512
+# main tiles, the 128 x 256 tile from 512, the 256 x 256 tile of the gradient
+# layouts from 512 such tiles and 2^17 tile x k-block units, and the
+# one-k-block stages for an odd number of k-blocks.
+DISPATCH = [
+    # (tA, tB, M, N, K, what)
+    (0, 0, 4096, 3840, 256, "480 main tiles: 64x128 tile"),
+    (0, 0, 4096, 4096, 256, "512 main tiles: 128x256 tile"),
+    (0, 1, 4096, 4096, 224, "odd k-block count (7): one-k-block stages"),
+    (1, 0, 32, 32, 32, "one block, one k-block"),
+    (1, 0, 8192, 4096, 8192, "512 big tiles x 256 k-blocks = 2^17: 256x256 tile"),
+    (1, 0, 8192, 4096, 8128, "512 big tiles x 254 k-blocks < 2^17: 128x256 tile"),
+    (0, 1, 8192, 3840, 8192, "480 big tiles: 128x256 tile"),
+    (1, 1, 8192, 4096, 8192, "both transposed, 256x256 tile"),
+]
+
+
+@pytest.mark.parametrize("ta,tb,M,N,K,what", DISPATCH, ids=[d[5] for d in DISPATCH])
+def test_dispatch_boundaries_every_element(ta, tb, M, N, K, what):
+    A, sA, B, sB = small_code_operands(1000 + M // 32 + N // 32 + K // 32, M, N, K, ta, tb)
+    note(f"dispatch {what}: {M}x{N}x{K} tA={ta} tB={tb}")
+    c, q, s = run_gemm(dev(A), dev(sA), dev(B), dev(sB), ta, tb, M, N)
+    exp32 = exact_expected(A, sA, B, sB, ta, tb)
+    frac, srel = check_exact(c, q, s, exp32, what)
+    note(f"  {M * N} elements exact; i8 code diffs {frac:.2e}")
