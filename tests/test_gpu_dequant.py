@@ -4,9 +4,10 @@ Bar: bit-exact (every output is one binary32 product, then for bfloat16 one
 nearest-even rounding).  Cases: every byte value, scales from subnormal
 products to the overflow edge of bfloat16, zero-scale blocks, block-column
 counts and row counts that leave a partial tail of the launch grid, strided
-input and output views (the padding must stay untouched), and the
+input and output views (the padding must stay untouched), the
 16384 x 16384 memory-bound workload's GELU output in full, with the data
-flow's error against the binary64 GELU of the original fp32 activation.
+flow's error against the binary64 GELU of the original fp32 activation, and
+the 64-bit index path (2^31 units of work) on sampled block rows.
 """
 import math
 
@@ -107,3 +108,27 @@ def test_memory_bound_gelu_output_bf16_copy():
         worst = max(worst, float(((yb - ref).abs() / bound).max()))
     note(f"dequantize memory-bound: bit-exact; worst error / bound vs binary64 GELU(x) = {worst:.3f}")
     assert worst <= 1.0
+
+
+@pytest.mark.parametrize("dtype,rows,cols", [(torch.float32, 1 << 17, 1 << 16), (torch.bfloat16, 1 << 18, 1 << 16)],
+                         ids=["f32-8Gi-elements", "bf16-16Gi-elements"])
+def test_64bit_unit_indices(dtype, rows, cols):
+    """At 2^31 units of work (4 codes per unit for binary32 output, 8 for
+    bfloat16) the launcher switches to 64-bit unit indices: 8 Gi codes to
+    binary32 (40 GB on the device) and 16 Gi codes to bfloat16 (48 GB).
+    Codes are drawn on the device; the first, a middle and the last block
+    rows are compared with the oracle bit for bit."""
+    note(f"dequantize 64-bit indices: {rows} x {cols} to {dtype}")
+    g = torch.Generator(device=DEV)
+    g.manual_seed(rows + cols)
+    q = torch.randint(-127, 128, (rows, cols), dtype=torch.int8, device=DEV, generator=g)
+    s = torch.rand((rows // 32, cols // 32), device=DEV, generator=g) * 0.01 + 1e-4
+    y = jf.dequantize_block(q, s, dtype=dtype)
+    torch.cuda.synchronize()
+    for bi in (0, rows // 64, rows // 32 - 1):
+        qh = host(q[32 * bi:32 * bi + 32])
+        sh = host(s[bi:bi + 1])
+        got = bits(y[32 * bi:32 * bi + 32])
+        np.testing.assert_array_equal(got, expected(qh, sh, dtype), err_msg=f"block row {bi}")
+    del q, s, y
+    torch.cuda.empty_cache()
