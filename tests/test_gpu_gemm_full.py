@@ -27,8 +27,8 @@
 5. 64-bit load offsets on the two large tiles: one operand with a leading
    dimension of 2^23 + 64 bytes, every element with the exact construction.
 6. Shapes on both sides of every tile-selection switch (grid sizes, the
-   256 x 256 tile's work threshold, odd k-block counts), every element with
-   the exact construction.
+   256 x 256 tile's work threshold, odd k-block counts), and 24 seeded random
+   small shapes in all layouts: every element with the exact construction.
 7. The GPT2-base linear (4096 tokens, 768 -> 3072) and the GPT2-medium MLP
    (8192 tokens, 1024 -> 4096 -> 1024): every GEMM on its workload's data,
    every element of both outputs against the oracle (grids of fewer than
@@ -310,3 +310,24 @@ def test_dispatch_boundaries_every_element(ta, tb, M, N, K, what):
     exp32 = exact_expected(A, sA, B, sB, ta, tb)
     frac, srel = check_exact(c, q, s, exp32, what)
     note(f"  {M * N} elements exact; i8 code diffs {frac:.2e}")
+
+
+def _sweep_shapes(n=24, seed=2024):
+    g = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        M, N = (int(v) * 32 for v in g.integers(1, 40, size=2))
+        K = int(g.integers(1, 70)) * 32
+        out.append((int(g.integers(0, 2)), int(g.integers(0, 2)), M, N, K))
+    return out
+
+
+@pytest.mark.parametrize("ta,tb,M,N,K", _sweep_shapes())
+def test_seeded_shape_sweep_every_element(ta, tb, M, N, K):
+    """Seeded random shapes up to 1248 x 1248 x 2208 in all four layouts
+    (small grids, ragged tiles, odd and even k-block counts): every element
+    with the exact construction."""
+    A, sA, B, sB = small_code_operands(2000 + M + 3 * N + 7 * K + ta + 2 * tb, M, N, K, ta, tb)
+    c, q, s = run_gemm(dev(A), dev(sA), dev(B), dev(sB), ta, tb, M, N)
+    exp32 = exact_expected(A, sA, B, sB, ta, tb)
+    check_exact(c, q, s, exp32, f"{M}x{N}x{K} tA={ta} tB={tb}")
