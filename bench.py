@@ -738,7 +738,8 @@ def gelu_copy_check(x, s1, qg, sg, y):
     Per element the data flow's error is bounded by the input quantization
     (|x - s1 q1| <= s1 (1/2 + 2e-5) with the quotient's rounding, times
     max |GELU'| < 1.13), the output code rounding (s2 (1/2 + 2e-5)) and the
-    bfloat16 rounding (2^-9 relative, 2^-8 with the binary32 roundings);
+    bfloat16 rounding (half an ulp of 8 significant bits: 2^-8 (1 + 2^-7)
+    relative to the rounded value);
     reported: the largest error over that bound, the largest error in output
     code units (err / s2) and the normwise relative error."""
     import torch
@@ -755,7 +756,7 @@ def gelu_copy_check(x, s1, qg, sg, y):
         e = (yb - g).abs()
         e1 = s1[r0 // 32:(r0 + 2048) // 32].double().repeat_interleave(32, 0).repeat_interleave(32, 1)
         e2 = sg[r0 // 32:(r0 + 2048) // 32].double().repeat_interleave(32, 0).repeat_interleave(32, 1)
-        bound = 1.13 * e1 * (0.5 + 2e-5) + e2 * (0.5 + 2e-5) + 2.0 ** -8 * yb.abs() + 1e-30
+        bound = 1.13 * e1 * (0.5 + 2e-5) + e2 * (0.5 + 2e-5) + 2.0 ** -8 * (1 + 2.0 ** -7) * yb.abs() + 1e-30
         worst_bound = max(worst_bound, float((e / bound).max()))
         worst_lsb = max(worst_lsb, float((e / torch.where(e2 > 0, e2, torch.ones_like(e2))).max()))
         num += float((e * e).sum())

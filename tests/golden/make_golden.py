@@ -75,6 +75,14 @@ def main():
         "Written by tests/golden/make_golden.py with the CPU oracle; " + RECIPE + ".",
     ], [("qdy", qd), ("sdy", sd), ("qx", qh), ("sx", sh), ("qo", qb), ("so", sb)])
 
+    write(os.path.join(HERE, "dequant_32x64.txt"), [
+        "Dequantization of per-block INT8 codes (the GELU output above, and quantize(X)): y = fl(s q) in",
+        "binary32, and its bfloat16 copy, the nearest bfloat16 of y with ties to even (raw 16-bit patterns).",
+        "Jetfire summary, \"Approach\" (INT8 tensors with one scale per 32x32 block).",
+        "Written by tests/golden/make_golden.py with the CPU oracle; " + RECIPE + ".",
+    ], [("q", qg), ("s", sg), ("y", oracle.dequantize(qg, sg)), ("ybf16", oracle.dequantize_bf16(qg, sg)),
+        ("qx", qx), ("sx", sx), ("yx", oracle.dequantize(qx, sx)), ("yxbf16", oracle.dequantize_bf16(qx, sx))])
+
 
 if __name__ == "__main__":
     main()

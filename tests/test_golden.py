@@ -58,3 +58,18 @@ def test_gelu_fixtures():
     qo, so = oracle.gelu_bwd(d["qdy"], d["sdy"], d["qx"], d["sx"])
     np.testing.assert_array_equal(qo, d["qo"])
     np.testing.assert_array_equal(so, d["so"])
+
+
+def test_dequant_fixture():
+    """The oracle reproduces the stored values, and the stored values hold the
+    definition checked independently: y equals the exact product s q wherever
+    it is representable (|q| s within binary32 with the product's bits), and
+    each bfloat16 pattern is the nearest bfloat16 to y (ties even)."""
+    d = read("dequant_32x64.txt")
+    for q, s, y, yb in (("q", "s", "y", "ybf16"), ("qx", "sx", "yx", "yxbf16")):
+        np.testing.assert_array_equal(oracle.dequantize(d[q], d[s]), d[y])
+        np.testing.assert_array_equal(oracle.dequantize_bf16(d[q], d[s]), d[yb])
+        exact = np.repeat(np.repeat(d[s].astype(np.float64), 32, 0), 32, 1) * d[q]
+        np.testing.assert_array_equal(d[y], exact.astype(np.float32))   # one rounding of the exact product
+        up = (d[yb].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        assert np.all(np.abs(up - d[y]) <= np.abs(d[y]) * 2.0 ** -8)   # half a bfloat16 ulp (8 bits)

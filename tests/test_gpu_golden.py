@@ -1,6 +1,6 @@
 """GPU parity on the stored fixtures of tests/golden/ (the oracle's outputs on
 seeded inputs, written by tests/golden/make_golden.py): quantize and the
-block-scaled GEMM (F32 and INT8 output) bit for bit, GELU and GELU backward
+block-scaled GEMM (F32 and INT8 output) and dequantization bit for bit, GELU and GELU backward
 to the requantization bar (codes within 1 LSB on at most 0.01% of elements,
 scales within 1e-6; the observed differences are printed)."""
 import numpy as np
@@ -38,3 +38,14 @@ def test_gelu_fixtures():
     qo, so = jf.gelu_bwd_i8(dev(d["qdy"]), dev(d["sdy"]), dev(d["qx"]), dev(d["sx"]))
     frac, srel = assert_requant_close(host(qo), host(so), d["qo"], d["so"], "gelu_bwd fixture")
     note(f"gelu_bwd fixture: code diffs {frac:.2e}, scale rel {srel:.1e}")
+
+
+def test_dequant_fixture():
+    import torch
+
+    d = read("dequant_32x64.txt")
+    for q, s, y, yb in (("q", "s", "y", "ybf16"), ("qx", "sx", "yx", "yxbf16")):
+        got = host(jf.dequantize_block(dev(d[q]), dev(d[s])))
+        np.testing.assert_array_equal(got.view(np.uint32), d[y].view(np.uint32))
+        gb = jf.dequantize_block(dev(d[q]), dev(d[s]), dtype=torch.bfloat16)
+        np.testing.assert_array_equal(host(gb.view(torch.int16)).view(np.uint16), d[yb])
