@@ -335,7 +335,9 @@ def bf16_reference(step, steps):
     """The same 12 GEMM shapes as plain bfloat16 GEMMs (torch.mm, i.e. the
     vendor BLAS), for the INT8-vs-bf16 comparison of the linear layers.
     Operands are laid out beforehand (no transposed views), outputs are bf16,
-    inputs random N(0,1); GEMMs only, nothing else of the step."""
+    inputs random N(0,1).  Returns (GEMMs only, GEMMs + the bf16 GELU of the
+    FC1 output and its backward): the second is the bf16 counterpart of the
+    INT8 step, which also runs its GELU, GELU backward and quantizations."""
     import torch
 
     dev = torch.device("cuda:0")
@@ -351,22 +353,34 @@ def bf16_reference(step, steps):
         C = torch.empty((m["M"], m["N"]), device=dev, dtype=torch.bfloat16)
         mats.append((A, B, C))
 
+    fc1 = step.meta["fc1.fwd"]
+    h = torch.randn((fc1["M"], fc1["N"]), device=dev, generator=g).to(torch.bfloat16)
+    dh = torch.randn((fc1["M"], fc1["N"]), device=dev, generator=g).to(torch.bfloat16)
+
     def run():
         for A, B, C in mats:
             torch.mm(A, B, out=C)
 
-    run()
-    torch.cuda.synchronize()
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for _ in range(steps):
+    def run_layer():
         run()
-    t1.record()
-    torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / steps
-    del mats
+        torch.nn.functional.gelu(h)                    # erf form
+        torch.ops.aten.gelu_backward(dh, h)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(steps):
+            fn()
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / steps
+
+    ms, layer_ms = timed(run), timed(run_layer)
+    del mats, h, dh
     torch.cuda.empty_cache()
-    return ms
+    return ms, layer_ms
 
 
 def int8_library_reference(step, steps):
@@ -860,11 +874,14 @@ def main():
 
     bf16 = None
     if args.bf16_steps > 0:
-        bms = bf16_reference(step, args.bf16_steps)
+        bms, blms = bf16_reference(step, args.bf16_steps)
         bf16 = {"ms_per_step": round(bms, 4), "tflops": round(step.gemm_ops / (bms * 1e-3) / 1e12, 2),
                 "int8_gemm_speedup": round(bms / gemm_ms, 3),
+                "layer_ms_per_step": round(blms, 4), "int8_step_speedup": round(blms / ms_step, 3),
                 "what": "the 12 GEMM shapes as torch.mm in bfloat16 (vendor BLAS), operands pre-laid-out, "
-                        "bf16 outputs; compared with the INT8 GEMMs' time in the step"}
+                        "bf16 outputs; compared with the INT8 GEMMs' time in the step. layer: the same GEMMs "
+                        "plus the bf16 GELU of the 8192x16384 FC1 output and its backward, against the whole "
+                        "INT8 step (its GEMMs, quantizations, GELU and GELU backward)"}
     i8lib = None
     if args.bf16_steps > 0:
         try:
