@@ -558,15 +558,26 @@ def mlp1024_section(reps=10):
         for A, B, C in mats:
             torch.mm(A, B, out=C)
 
+    h = torch.randn((8192, 4096), device=dev, generator=g).to(torch.bfloat16)
+    dh = torch.randn((8192, 4096), device=dev, generator=g).to(torch.bfloat16)
+
+    def bf16_layer():
+        bf16()
+        torch.nn.functional.gelu(h)
+        torch.ops.aten.gelu_backward(dh, h)
+
     bf_us = _time_us(bf16, reps)
-    del mats, q, fp
+    bfl_us = _time_us(bf16_layer, reps)
+    del mats, q, fp, h, dh
     torch.cuda.empty_cache()
     return {"int8_step_ms": round(step_us / 1e3, 4), "int8_step_tops": round(ops / (step_us * 1e-6) / 1e12, 1),
             "int8_gemm_ms": round(gemm_us / 1e3, 4), "int8_gemm_tops": round(ops / (gemm_us * 1e-6) / 1e12, 1),
             "bf16_gemm_ms": round(bf_us / 1e3, 4), "bf16_tflops": round(ops / (bf_us * 1e-6) / 1e12, 1),
             "int8_gemm_speedup": round(bf_us / gemm_us, 3), "gemm_ops": ops,
+            "bf16_layer_ms": round(bfl_us / 1e3, 4), "int8_step_speedup": round(bfl_us / step_us, 3),
             "what": "GPT2-medium-like MLP, 8192 tokens, 1024->4096->1024: INT8 data flow (13 kernels) and its "
-                    "6 INT8 GEMMs vs the same 6 GEMM shapes as torch.mm in bfloat16"}
+                    "6 INT8 GEMMs vs the same 6 GEMM shapes as torch.mm in bfloat16; bf16 layer: those GEMMs "
+                    "plus the bf16 GELU of the 8192x4096 FC1 output and its backward, against the INT8 data flow"}
 
 
 CEIL = {"mfma_only": 0, "mfma_rescale": 1, "mfma_bias_rescale": 2, "copy_i8": 3, "copy_f32_to_i8": 4,
