@@ -26,7 +26,8 @@ from int8_block_quantized_amd import inputs  # noqa: E402
 WID = 90
 RECIPE = ("inputs: int8_block_quantized_amd.inputs, workload id 90; X = activation(90, 0, 32, 64, "
           "2 columns x100), H = activation(90, 1, 32, 64, 2 columns x100), W = normal(90, W, 0, 64, 32, "
-          "std 0.02), dY = normal(90, dY, 0, 32, 64, std 1e-3)")
+          "std 0.02), dY = normal(90, dY, 0, 32, 64, std 1e-3), gamma = 1 + normal(90, W, 5, 1, 64, std 0.1), "
+          "beta = normal(90, W, 6, 1, 64, std 0.1)")
 
 
 def main():
@@ -82,6 +83,39 @@ def main():
         "Written by tests/golden/make_golden.py with the CPU oracle; " + RECIPE + ".",
     ], [("q", qg), ("s", sg), ("y", oracle.dequantize(qg, sg)), ("ybf16", oracle.dequantize_bf16(qg, sg)),
         ("qx", qx), ("sx", sx), ("yx", oracle.dequantize(qx, sx)), ("yxbf16", oracle.dequantize_bf16(qx, sx))])
+
+    qa, sa = oracle.add(qx, sx, qh, sh)
+    write(os.path.join(HERE, "add_32x64.txt"), [
+        "Residual add of two per-block INT8 tensors (quantize(X) and quantize(H)): z = fl(fl(sa qa) + fl(sb qb)),",
+        "then the per-block rule on z.",
+        "Jetfire summary, \"Approach\" (every operator of the data flow on INT8 with block scales); the add is",
+        "this library's reading.",
+        "Written by tests/golden/make_golden.py with the CPU oracle; " + RECIPE + ".",
+    ], [("qa", qx), ("sa", sx), ("qb", qh), ("sb", sh), ("qo", qa), ("so", sa)])
+
+    gamma = (1.0 + inputs.normal(WID, inputs.TAG_W, 5, 1, 64, 0.1)).astype(np.float32).ravel()
+    beta = inputs.normal(WID, inputs.TAG_W, 6, 1, 64, 0.1).ravel()
+    qn, sn, mean, rstd = oracle.layernorm(qx, sx, gamma, beta, 1e-5, stats=True)
+    write(os.path.join(HERE, "layernorm_32x64.txt"), [
+        "LayerNorm over each row of quantize(X), eps = 1e-5: x = fl(s q); mean and biased variance in binary64",
+        "(column order); r = 1/sqrt(v + eps); y = ((x - m) r) gamma + beta in binary64 rounded once to binary32;",
+        "then the per-block rule on y (qo, so); the row means and r (binary64).",
+        "Jetfire summary, \"Approach\" (INT8 data flow); the normalization is this library's reading.",
+        "Written by tests/golden/make_golden.py with the CPU oracle; " + RECIPE + ".",
+    ], [("q", qx), ("s", sx), ("gamma", gamma), ("beta", beta), ("qo", qn), ("so", sn), ("mean", mean),
+        ("rstd", rstd)])
+
+    arrays = [("x", x)]
+    for gname in ("block", "token", "channel", "tensor"):
+        sg_, sse = oracle.quant_sse(x, gname)
+        arrays += [(f"s_{gname}", sg_), (f"sse_{gname}", np.array([sse], np.float64))]
+    write(os.path.join(HERE, "qerror_32x64.txt"), [
+        "Quantization error of X under four scale granularities (32x32 block, token = row, channel = column,",
+        "tensor): the per-group scale s = fl(max|x| / 127), and sum (x - fl(s q))^2 over all elements, each term",
+        "in binary64, added in row order.",
+        "Jetfire summary, \"Measured effects\" (per-block against per-token and per-channel quantization error).",
+        "Written by tests/golden/make_golden.py with the CPU oracle; " + RECIPE + ".",
+    ], arrays)
 
 
 if __name__ == "__main__":

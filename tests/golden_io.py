@@ -2,8 +2,8 @@
 
 A fixture file holds comment lines (starting with '#') and arrays, each
 introduced by a line 'array <name> <dtype> <rows> <cols>' and followed by its
-values in row-major order, whitespace-separated.  float32 values are written
-as C99 hex floats (exact), integers in decimal.
+values in row-major order, whitespace-separated.  float32 and float64 values
+are written as C99 hex floats (exact), integers in decimal.
 """
 import os
 
@@ -18,7 +18,7 @@ def write(path, header_lines, arrays):
             f.write(f"# {line}\n" if line else "#\n")
         for name, a in arrays:
             a = np.atleast_2d(np.asarray(a))
-            if a.dtype == np.float32:
+            if a.dtype in (np.float32, np.float64):
                 vals = [float(v).hex() for v in a.ravel()]
             else:
                 vals = [str(int(v)) for v in a.ravel()]
@@ -41,8 +41,8 @@ def read(name):
             vals.extend(line.split())
             if len(vals) == want:
                 nm, dt, r, c = cur
-                if dt == np.float32:
-                    a = np.array([float.fromhex(v) for v in vals], dtype=np.float32)
+                if dt in (np.float32, np.float64):
+                    a = np.array([float.fromhex(v) for v in vals], dtype=dt)
                 else:
                     a = np.array([int(v) for v in vals], dtype=dt)
                 out[nm] = a.reshape(r, c)

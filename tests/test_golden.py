@@ -73,3 +73,32 @@ def test_dequant_fixture():
         np.testing.assert_array_equal(d[y], exact.astype(np.float32))   # one rounding of the exact product
         up = (d[yb].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
         assert np.all(np.abs(up - d[y]) <= np.abs(d[y]) * 2.0 ** -8)   # half a bfloat16 ulp (8 bits)
+
+
+def test_add_layernorm_qerror_fixtures():
+    """The oracle reproduces the stored add, LayerNorm and quantization-error
+    values bit for bit, and the stored values keep their defining
+    invariants: every LayerNorm row has mean ~0 and unit variance before the
+    affine map (checked on the stored row statistics against the dequantized
+    input), and each granularity's error sum is at most n (s/2)^2 for its
+    largest scale."""
+    d = read("add_32x64.txt")
+    qo, so = oracle.add(d["qa"], d["sa"], d["qb"], d["sb"])
+    np.testing.assert_array_equal(qo, d["qo"])
+    np.testing.assert_array_equal(so, d["so"])
+    d = read("layernorm_32x64.txt")
+    qo, so, mean, rstd = oracle.layernorm(d["q"], d["s"], d["gamma"].ravel(), d["beta"].ravel(), 1e-5, stats=True)
+    np.testing.assert_array_equal(qo, d["qo"])
+    np.testing.assert_array_equal(so, d["so"])
+    np.testing.assert_array_equal(mean, d["mean"].ravel())
+    np.testing.assert_array_equal(rstd, d["rstd"].ravel())
+    x = oracle.dequantize(d["q"], d["s"]).astype(np.float64)
+    np.testing.assert_allclose(d["mean"].ravel(), x.mean(axis=1), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(d["rstd"].ravel(), 1.0 / np.sqrt(x.var(axis=1) + np.float64(np.float32(1e-5))),
+                               rtol=1e-12)
+    d = read("qerror_32x64.txt")
+    for g in ("block", "token", "channel", "tensor"):
+        s, sse = oracle.quant_sse(d["x"], g)
+        np.testing.assert_array_equal(s, d[f"s_{g}"].ravel())
+        assert sse == float(d[f"sse_{g}"][0, 0])
+        assert sse <= d["x"].size * (float(s.max()) / 2) ** 2
